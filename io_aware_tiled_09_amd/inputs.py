@@ -1,0 +1,162 @@
+"""Seeded synthetic attention inputs.
+
+This module only draws random numbers, shapes them like the workloads the
+FlashAttention pages talk about, and casts them to the storage dtype. It holds
+none of the attention arithmetic, so both the HIP path and the CPU oracle can
+take their inputs from here without sharing any computation.
+
+Workloads (stand-ins for the pages' examples; no dataset or weights exist here):
+
+* ``single_head``   one head, N=256, d=64, fp32 storage, non-causal.
+* ``bert512``       BERT-shaped self-attention, B=4, H=12, N=512, d=64.
+                    [FlashAttention: The GPU Memory Hack That Changed Everything,
+                    "The Numbers: Speed and Memory", BERT (seq 512) row]
+* ``gpt2_1k``       GPT-2-shaped causal attention, B=8, H=12, N=1024, d=64.
+                    [same page and table, GPT-2 (seq 1K) row]
+* ``gpt2_1k_spiky`` the same with 1% of the key rows multiplied by 20, so the
+                    running maximum of the online softmax moves often.
+* ``longdoc8k``     long-document causal attention, B=2, H=32, N=8192, d=128.
+                    [Flash Attention Optimization (aicomputerinstitute.com),
+                    opening section: 8,000-30,000-token documents]
+* ``longctx32k``    very long context, B=1, H=32, N=32768, d=128, entries
+                    N(0, 0.5^2) times one U[0.5, 2] factor per head.
+
+All draws come from ``torch.Generator('cpu').manual_seed(seed)`` in the order
+Q, K, V, then the variant's extra draws, in fp32; bf16 storage is the
+round-to-nearest-even cast of those fp32 values. The tensors returned are the
+exact values both the GPU and the oracle consume.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "sample_rows", "useful_flops"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str  # "bf16" or "fp32" (storage dtype of q, k, v and o)
+    seed: int
+    std: float = 1.0
+    spike_frac: float = 0.0  # fraction of K rows (over flattened b, h, j) scaled
+    spike_factor: float = 1.0
+    head_scale: tuple | None = None  # (lo, hi): one U[lo, hi] factor per head
+    oracle_rows: int | None = None  # rows per head the oracle checks; None = all
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("single_head", 1, 1, 256, 64, False, "fp32", 1000,
+                 note="single head, fp32 storage"),
+        Workload("bert512", 4, 12, 512, 64, False, "bf16", 1001,
+                 note="BERT-shaped self-attention"),
+        Workload("gpt2_1k", 8, 12, 1024, 64, True, "bf16", 1002,
+                 note="GPT-2-shaped causal attention"),
+        Workload("gpt2_1k_spiky", 8, 12, 1024, 64, True, "bf16", 1003,
+                 spike_frac=0.01, spike_factor=20.0,
+                 note="GPT-2 shape, 1% of K rows x20"),
+        Workload("longdoc8k", 2, 32, 8192, 128, True, "bf16", 1004,
+                 note="long-document causal attention"),
+        Workload("longctx32k", 1, 32, 32768, 128, True, "bf16", 1005,
+                 std=0.5, head_scale=(0.5, 2.0), oracle_rows=256,
+                 note="very long context, per-head scale"),
+    ]
+}
+
+
+def _cast(x: torch.Tensor, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)  # round to nearest even
+    if dtype == "fp32":
+        return x.contiguous()
+    raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+def make_qkv(w: Workload | str | None = None, *, B=None, H=None, N=None, d=None,
+             dtype=None, seed=None, std=None):
+    """Return contiguous CPU tensors ``(q, k, v)`` of shape [B, H, N, d].
+
+    Either name a workload (its fields may be overridden by keyword) or give
+    the shape, dtype and seed directly. Entries are i.i.d. N(0, std^2) fp32
+    draws, then the workload's variant draws, then the storage cast.
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if w is None:
+        w = Workload("custom", B, H, N, d, False, dtype or "bf16",
+                     0 if seed is None else seed, std=1.0 if std is None else std)
+    else:
+        over = {k_: v_ for k_, v_ in dict(B=B, H=H, N=N, d=d, dtype=dtype,
+                                           seed=seed, std=std).items()
+                if v_ is not None}
+        if over:
+            w = Workload(**{**w.__dict__, **over})
+    g = torch.Generator(device="cpu").manual_seed(int(w.seed))
+    shape = (w.B, w.H, w.N, w.d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if w.std != 1.0:
+        q.mul_(w.std)
+        k.mul_(w.std)
+        v.mul_(w.std)
+    if w.spike_frac > 0.0:
+        rows = w.B * w.H * w.N
+        count = int(round(w.spike_frac * rows))
+        idx = torch.randperm(rows, generator=g)[:count]
+        k.view(rows, w.d)[idx] *= w.spike_factor
+    if w.head_scale is not None:
+        lo, hi = w.head_scale
+        c = torch.rand(w.H, generator=g, dtype=torch.float32) * (hi - lo) + lo
+        c = c.view(1, w.H, 1, 1)
+        q.mul_(c)
+        k.mul_(c)
+        v.mul_(c)
+    return _cast(q, w.dtype), _cast(k, w.dtype), _cast(v, w.dtype)
+
+
+def sample_rows(N: int, count: int, seed: int, heads: int = 1) -> torch.Tensor:
+    """Seeded, sorted sample of ``count`` distinct query rows per head.
+
+    Rows 0 and N-1 are always in the sample; the rest are drawn without
+    replacement. Returns int64 [heads, min(count, N)].
+    """
+    count = min(count, N)
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = torch.empty((heads, count), dtype=torch.int64)
+    for h in range(heads):
+        if count == N:
+            out[h] = torch.arange(N)
+            continue
+        fixed = [0, N - 1] if N > 1 else [0]
+        inner = torch.randperm(N - 2, generator=g)[: count - len(fixed)] + 1 \
+            if N > 2 else torch.empty(0, dtype=torch.int64)
+        rows = torch.cat([torch.tensor(fixed, dtype=torch.int64), inner])
+        out[h] = torch.sort(rows).values
+    return out
+
+
+def useful_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Useful FLOPs of one forward call: 2*N*N*d for QK^T plus 2*N*N*d for PV
+    per head, halved when causal (only keys j <= i count)."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2.0 if causal else f

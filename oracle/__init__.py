@@ -1,0 +1,180 @@
+"""Attention-forward oracle (fp64, CPU): TEST INFRASTRUCTURE, not the product.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It loads ``liboracle.so``, built from
+``oracle.c`` with gcc (OpenMP, no fast-math); it shares no code with the HIP
+path and the HIP path never imports it.
+
+Every function takes and returns float64 numpy arrays. Inputs handed to the
+GPU in bf16 or fp32 are upcast exactly to float64 before they get here.
+
+Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
+
+* ``softmax_row``: the worked examples printed on the pages, closed forms.
+* ``online_row_two_scale`` / ``online_row_single_max``: the worked examples
+  (final outputs and block states), brute force against ``softmax_row`` for
+  every block size on tiny rows.
+* ``attention_fwd`` / ``attention_rows``: closed forms (N = 1, Q = 0, causal
+  row 0), invariances (key/value permutation, value scaling, per-row score
+  shift), rows of P summing to 1, and torch's CPU float64 scaled dot-product
+  attention and logsumexp on random inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_lp = ctypes.POINTER(ctypes.c_long)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` (always recompiles)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+           "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_softmax_row.argtypes = [_dp, _dp, ctypes.c_long, ctypes.c_long, _dp, _dp]
+    for name in ("oracle_online_row_two_scale", "oracle_online_row_single_max"):
+        getattr(lib, name).argtypes = [_dp, _dp, ctypes.c_long, ctypes.c_long,
+                                       ctypes.c_long, _dp, _dp, _dp]
+    lib.oracle_attention_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp,
+                                         ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                         ctypes.c_long, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attention_rows.argtypes = [_dp, _dp, _dp, ctypes.c_long, ctypes.c_long,
+                                          ctypes.c_long, ctypes.c_long, ctypes.c_double,
+                                          ctypes.c_int, _lp, ctypes.c_long, _dp, _dp]
+    for name in ("oracle_softmax_row", "oracle_online_row_two_scale",
+                 "oracle_online_row_single_max", "oracle_attention_fwd",
+                 "oracle_attention_rows"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # a torch tensor: exact upcast on the CPU
+        import torch
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
+
+
+def _row_args(s, v):
+    s = _f64(s).reshape(-1)
+    v = _f64(v)
+    if v.ndim == 1:
+        v = v.reshape(-1, 1)
+    if v.shape[0] != s.shape[0]:
+        raise ValueError("scores and values disagree in length")
+    return s, np.ascontiguousarray(v)
+
+
+def softmax_row(s, v):
+    """Direct softmax-weighted sum of one row; returns (out[dv], lse)."""
+    s, v = _row_args(s, v)
+    out = np.empty(v.shape[1])
+    lse = ctypes.c_double()
+    _check(_load().oracle_softmax_row(_ptr(s), _ptr(v), s.size, v.shape[1], _ptr(out),
+                                      ctypes.byref(lse)), "softmax_row")
+    return out, lse.value
+
+
+def _online(name, s, v, block):
+    s, v = _row_args(s, v)
+    out = np.empty(v.shape[1])
+    m = ctypes.c_double()
+    l_ = ctypes.c_double()
+    _check(getattr(_load(), name)(_ptr(s), _ptr(v), s.size, v.shape[1], int(block),
+                                  _ptr(out), ctypes.byref(m), ctypes.byref(l_)), name)
+    return out, m.value, l_.value
+
+
+def online_row_two_scale(s, v, block):
+    """Block-local online softmax (two correction factors); (out, m, l)."""
+    return _online("oracle_online_row_two_scale", s, v, block)
+
+
+def online_row_single_max(s, v, block):
+    """Single running-max online softmax; (out, m, l)."""
+    return _online("oracle_online_row_single_max", s, v, block)
+
+
+def attention_fwd(q, k, v, scale, causal, return_p=False):
+    """Standard attention on [B, H, N, d] inputs, S and P materialized.
+
+    Returns (o [B,H,N,d], lse [B,H,N]) or, with return_p, also P [B,H,N,N].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if not (q.shape == k.shape == v.shape) or q.ndim != 4:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N))
+    p = np.empty((B, H, N, N)) if return_p else None
+    _check(_load().oracle_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        _ptr(p) if p is not None else None,
+                                        B, H, N, d, float(scale), int(bool(causal))),
+           "attention_fwd")
+    return (o, lse, p) if return_p else (o, lse)
+
+
+def attention_rows(q, k, v, scale, causal, rows):
+    """Standard attention for selected rows.
+
+    rows: int array [B*H, R] (or [R], the same rows for every head).
+    Returns (o_rows [B*H, R, d], lse_rows [B*H, R]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if not (q.shape == k.shape == v.shape) or q.ndim != 4:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    r = np.asarray(rows.numpy() if hasattr(rows, "numpy") else rows, dtype=np.int64)
+    if r.ndim == 1:
+        r = np.broadcast_to(r, (B * H, r.size))
+    r = np.ascontiguousarray(r, dtype=np.int64)
+    if r.shape[0] != B * H:
+        raise ValueError("rows must have one row list per head")
+    R = r.shape[1]
+    o = np.empty((B * H, R, d))
+    lse = np.empty((B * H, R))
+    _check(_load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), B, H, N, d,
+                                         float(scale), int(bool(causal)),
+                                         r.ctypes.data_as(_lp), R, _ptr(o), _ptr(lse)),
+           "attention_rows")
+    return o, lse

@@ -1,0 +1,353 @@
+/*
+ * Attention-forward oracle: TEST INFRASTRUCTURE, not part of the product.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library. It shares no code, header or constant with the HIP
+ * path, and the HIP path never calls it.
+ *
+ * Everything is plain fp64 C, built without fast-math, so a reader can check
+ * each function against the passage it cites:
+ *
+ *   [P1] "FlashAttention: The GPU Memory Hack That Changed Everything"
+ *        (ai.branddocks.com, episode 75)
+ *   [P2] "Flash Attention Optimization" chapter (aicomputerinstitute.com)
+ *
+ * Conventions (readings of points the pages leave open):
+ *   - tensors are contiguous [B][H][N][d], one (b, h) pair = one "head";
+ *   - scores carry an explicit `scale` (the pages use 1/sqrt(d));
+ *   - causal means key j is visible to query i iff j <= i (square
+ *     self-attention), so every row sees at least key 0;
+ *   - lse is the natural-log log-sum-exp of the scaled, masked scores,
+ *     lse_i = m_i + ln(l_i).
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_NOMEM 2
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Direct softmax-weighted sum for one query row: subtract the global max,
+ * exponentiate, normalize, then weight the values.
+ * [P2, "Worked example: online softmax by hand", the direct computation]
+ * [P2, "Attention is not slow because of arithmetic": P = softmax(S), O = P V]
+ *
+ * s: n scores; v: n value vectors of length dv (row-major [n][dv]);
+ * out: dv outputs; lse (may be NULL): m + ln(sum).
+ * Scores equal to -INFINITY (masked keys) get weight 0; at least one score
+ * must be finite.
+ */
+int oracle_softmax_row(const double *s, const double *v, long n, long dv,
+                       double *out, double *lse)
+{
+    if (!s || !v || !out || n < 1 || dv < 1)
+        return ORACLE_ERR_ARG;
+    double m = -INFINITY;
+    for (long j = 0; j < n; ++j)
+        if (s[j] > m)
+            m = s[j];
+    if (!(m > -INFINITY))
+        return ORACLE_ERR_ARG;
+    double *p = (double *)malloc((size_t)n * sizeof(double));
+    if (!p)
+        return ORACLE_ERR_NOMEM;
+    double sum = 0.0;
+    for (long j = 0; j < n; ++j) {
+        p[j] = exp(s[j] - m);
+        sum += p[j];
+    }
+    for (long j = 0; j < n; ++j)
+        p[j] /= sum;
+    for (long t = 0; t < dv; ++t)
+        out[t] = 0.0;
+    for (long j = 0; j < n; ++j)
+        for (long t = 0; t < dv; ++t)
+            out[t] += p[j] * v[j * dv + t];
+    if (lse)
+        *lse = m + log(sum);
+    free(p);
+    return ORACLE_OK;
+}
+
+/*
+ * Online softmax, block-local form with two correction factors, for one row.
+ * [P2, "The fix: tile the computation, never materialize the full matrix"]
+ * [P2, "Tracing the algorithm as code"]
+ *
+ * For every block of `block` consecutive scores: local max, exponentials
+ * relative to it, local sum and local weighted sum; then merge into the
+ * running (m, l, acc) with exp(m_old - m_new) and exp(m_block - m_new).
+ * Before the first block m = -inf, l = 0, acc = 0, so exp(m_old - m_new) is
+ * exactly 0 there. Output is acc / l.
+ *
+ * Reading for a case the pages do not cover: a block whose scores are all
+ * -inf (all masked) contributes nothing, instead of producing exp(-inf+inf).
+ * m_out / l_out (may be NULL) receive the final running max and sum.
+ */
+int oracle_online_row_two_scale(const double *s, const double *v, long n,
+                                long dv, long block, double *out,
+                                double *m_out, double *l_out)
+{
+    if (!s || !v || !out || n < 1 || dv < 1 || block < 1)
+        return ORACLE_ERR_ARG;
+    double *acc = (double *)calloc((size_t)dv, sizeof(double));
+    double *acc_blk = (double *)malloc((size_t)dv * sizeof(double));
+    if (!acc || !acc_blk) {
+        free(acc);
+        free(acc_blk);
+        return ORACLE_ERR_NOMEM;
+    }
+    double m = -INFINITY, l = 0.0;
+    for (long start = 0; start < n; start += block) {
+        long end = start + block < n ? start + block : n;
+        double m_blk = -INFINITY;
+        for (long j = start; j < end; ++j)
+            if (s[j] > m_blk)
+                m_blk = s[j];
+        if (!(m_blk > -INFINITY))
+            continue; /* fully masked block */
+        double l_blk = 0.0;
+        for (long t = 0; t < dv; ++t)
+            acc_blk[t] = 0.0;
+        for (long j = start; j < end; ++j) {
+            double p = exp(s[j] - m_blk);
+            l_blk += p;
+            for (long t = 0; t < dv; ++t)
+                acc_blk[t] += p * v[j * dv + t];
+        }
+        double m_new = m > m_blk ? m : m_blk;
+        double scale_old = exp(m - m_new);
+        double scale_new = exp(m_blk - m_new);
+        l = l * scale_old + l_blk * scale_new;
+        for (long t = 0; t < dv; ++t)
+            acc[t] = acc[t] * scale_old + acc_blk[t] * scale_new;
+        m = m_new;
+    }
+    int rc = ORACLE_OK;
+    if (!(l > 0.0))
+        rc = ORACLE_ERR_ARG; /* every score was -inf */
+    else
+        for (long t = 0; t < dv; ++t)
+            out[t] = acc[t] / l;
+    if (m_out)
+        *m_out = m;
+    if (l_out)
+        *l_out = l;
+    free(acc);
+    free(acc_blk);
+    return rc;
+}
+
+/*
+ * Online softmax, single running-max form, for one row.
+ * [P1, "FlashAttention: IO-Aware Tiling" / "The Tiling Strategy", the
+ *  pseudocode's inner loop, and "The Online Softmax Trick"]
+ *
+ * Per block: block max, new running max m_new = max(m, block max);
+ * l = l*exp(m - m_new) + sum(exp(s - m_new));
+ * O = O*exp(m - m_new) + sum(exp(s - m_new) * v); m = m_new.
+ * After the last block the output is O / l.
+ * Reading: a block with every score -inf leaves m unchanged and adds 0
+ * (exp(-inf - m) = 0); if m is still -inf there, the block is skipped.
+ */
+int oracle_online_row_single_max(const double *s, const double *v, long n,
+                                 long dv, long block, double *out,
+                                 double *m_out, double *l_out)
+{
+    if (!s || !v || !out || n < 1 || dv < 1 || block < 1)
+        return ORACLE_ERR_ARG;
+    double *o = (double *)calloc((size_t)dv, sizeof(double));
+    if (!o)
+        return ORACLE_ERR_NOMEM;
+    double m = -INFINITY, l = 0.0;
+    for (long start = 0; start < n; start += block) {
+        long end = start + block < n ? start + block : n;
+        double m_blk = -INFINITY;
+        for (long j = start; j < end; ++j)
+            if (s[j] > m_blk)
+                m_blk = s[j];
+        double m_new = m > m_blk ? m : m_blk;
+        if (!(m_new > -INFINITY))
+            continue; /* nothing visible yet */
+        double corr = exp(m - m_new);
+        double sum = 0.0;
+        for (long j = start; j < end; ++j)
+            sum += exp(s[j] - m_new);
+        l = l * corr + sum;
+        for (long t = 0; t < dv; ++t) {
+            double pv = 0.0;
+            for (long j = start; j < end; ++j)
+                pv += exp(s[j] - m_new) * v[j * dv + t];
+            o[t] = o[t] * corr + pv;
+        }
+        m = m_new;
+    }
+    int rc = ORACLE_OK;
+    if (!(l > 0.0))
+        rc = ORACLE_ERR_ARG;
+    else
+        for (long t = 0; t < dv; ++t)
+            out[t] = o[t] / l;
+    if (m_out)
+        *m_out = m;
+    if (l_out)
+        *l_out = l;
+    free(o);
+    return rc;
+}
+
+/*
+ * One query row of standard attention, materializing that row of S and P.
+ * S[j] = scale * sum_t Q[i][t] K[j][t]; causal: S[j] = -inf for j > i;
+ * P[j] = exp(S[j] - max S) / sum_j exp(S[j] - max S); O[i] = sum_j P[j] V[j];
+ * lse_i = max S + ln(sum_j exp(S[j] - max S)).
+ * [P1, "Standard Attention: The Memory-Wasteful Way", steps 1-3]
+ * [P2, "Attention is not slow because of arithmetic": S = QK^T/sqrt(d),
+ *  P = softmax(S) row-wise, O = P V]
+ * [P1, "Integration": is_causal=True]
+ */
+static void attention_row(const double *q, const double *k, const double *v,
+                          long N, long d, double scale, int causal, long i,
+                          double *S, double *P, double *o_row, double *lse)
+{
+    const double *qi = q + i * d;
+    /* step 1: one row of S = scale * Q K^T */
+    for (long j = 0; j < N; ++j) {
+        const double *kj = k + j * d;
+        double dot = 0.0;
+        for (long t = 0; t < d; ++t)
+            dot += qi[t] * kj[t];
+        S[j] = scale * dot;
+    }
+    /* causal mask: keys after the query are invisible */
+    if (causal)
+        for (long j = i + 1; j < N; ++j)
+            S[j] = -INFINITY;
+    /* step 2: row softmax with the global row max subtracted */
+    double m = -INFINITY;
+    for (long j = 0; j < N; ++j)
+        if (S[j] > m)
+            m = S[j];
+    double l = 0.0;
+    for (long j = 0; j < N; ++j) {
+        P[j] = exp(S[j] - m);
+        l += P[j];
+    }
+    for (long j = 0; j < N; ++j)
+        P[j] /= l;
+    /* step 3: O row = P row times V */
+    for (long t = 0; t < d; ++t)
+        o_row[t] = 0.0;
+    for (long j = 0; j < N; ++j) {
+        const double *vj = v + j * d;
+        const double pj = P[j];
+        for (long t = 0; t < d; ++t)
+            o_row[t] += pj * vj[t];
+    }
+    *lse = m + log(l);
+}
+
+/*
+ * Standard attention for every (b, h): materializes the full N x N score
+ * matrix S and probability matrix P of one head at a time, then O = P V.
+ * [P1, "Standard Attention: The Memory-Wasteful Way"]
+ * [P2, "Attention is not slow because of arithmetic"]
+ *
+ * q, k, v, o: [B][H][N][d] fp64; lse: [B][H][N] fp64;
+ * p_out: NULL, or [B][H][N][N] fp64 to receive P.
+ * Rows of a head are computed in parallel (OpenMP); each row's arithmetic is
+ * the sequential definition above, so the result does not depend on the
+ * thread count.
+ */
+int oracle_attention_fwd(const double *q, const double *k, const double *v,
+                         double *o, double *lse, double *p_out, long B, long H,
+                         long N, long d, double scale, int causal)
+{
+    if (B < 0 || H < 0 || N < 0 || d < 1)
+        return ORACLE_ERR_ARG;
+    if (B == 0 || H == 0 || N == 0)
+        return ORACLE_OK;
+    if (!q || !k || !v || !o || !lse || !isfinite(scale))
+        return ORACLE_ERR_ARG;
+    double *S = (double *)malloc((size_t)N * (size_t)N * sizeof(double));
+    double *P = (double *)malloc((size_t)N * (size_t)N * sizeof(double));
+    if (!S || !P) {
+        free(S);
+        free(P);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (long bh = 0; bh < B * H; ++bh) {
+        const size_t off = (size_t)bh * (size_t)N * (size_t)d;
+        const double *qh = q + off, *kh = k + off, *vh = v + off;
+        double *oh = o + off;
+        double *lh = lse + (size_t)bh * (size_t)N;
+#pragma omp parallel for schedule(dynamic, 4)
+        for (long i = 0; i < N; ++i)
+            attention_row(qh, kh, vh, N, d, scale, causal, i,
+                          S + (size_t)i * N, P + (size_t)i * N,
+                          oh + (size_t)i * d, lh + i);
+        if (p_out)
+            memcpy(p_out + (size_t)bh * (size_t)N * (size_t)N, P,
+                   (size_t)N * (size_t)N * sizeof(double));
+    }
+    free(S);
+    free(P);
+    return ORACLE_OK;
+}
+
+/*
+ * Standard attention for selected query rows only: the same definition as
+ * oracle_attention_fwd, materializing S and P one row at a time.
+ * rows: [B*H][R] query indices (0 <= row < N) per head;
+ * o_rows: [B*H][R][d]; lse_rows: [B*H][R].
+ */
+int oracle_attention_rows(const double *q, const double *k, const double *v,
+                          long B, long H, long N, long d, double scale,
+                          int causal, const long *rows, long R, double *o_rows,
+                          double *lse_rows)
+{
+    if (B < 1 || H < 1 || N < 1 || d < 1 || R < 0)
+        return ORACLE_ERR_ARG;
+    if (R == 0)
+        return ORACLE_OK;
+    if (!q || !k || !v || !rows || !o_rows || !lse_rows || !isfinite(scale))
+        return ORACLE_ERR_ARG;
+    for (long x = 0; x < B * H * R; ++x)
+        if (rows[x] < 0 || rows[x] >= N)
+            return ORACLE_ERR_ARG;
+    int nt = oracle_num_threads();
+    double *scratch = (double *)malloc((size_t)nt * 2 * (size_t)N * sizeof(double));
+    if (!scratch)
+        return ORACLE_ERR_NOMEM;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (long bh = 0; bh < B * H; ++bh)
+        for (long r = 0; r < R; ++r) {
+            int tid = 0;
+#ifdef _OPENMP
+            tid = omp_get_thread_num();
+#endif
+            double *S = scratch + (size_t)tid * 2 * (size_t)N;
+            double *P = S + N;
+            const size_t off = (size_t)bh * (size_t)N * (size_t)d;
+            const long i = rows[bh * R + r];
+            attention_row(q + off, k + off, v + off, N, d, scale, causal, i,
+                          S, P, o_rows + ((size_t)bh * R + r) * (size_t)d,
+                          lse_rows + (size_t)bh * R + r);
+        }
+    free(scratch);
+    return ORACLE_OK;
+}
