@@ -1,0 +1,89 @@
+/*
+ * fa.h: C ABI of the FlashAttention forward library (libfa.so, gfx950).
+ *
+ * The operation is exact softmax attention for every (batch, head):
+ *
+ *     S = scale * Q K^T          (N x N, never stored)
+ *     P = softmax(S) row-wise    (causal: key j visible to query i iff j <= i)
+ *     O = P V
+ *     lse_i = ln sum_j exp(S_ij)  over the visible keys j
+ *
+ * [FlashAttention: The GPU Memory Hack That Changed Everything
+ *  (ai.branddocks.com, episode 75), "Standard Attention" for S, P, O and
+ *  "FlashAttention: IO-Aware Tiling" for the tiled evaluation]
+ * [Flash Attention Optimization (aicomputerinstitute.com), "Attention is not
+ *  slow because of arithmetic" for S = QK^T / sqrt(d); "Sizing a tile, and
+ *  why the backward pass recomputes" for keeping per-row statistics (lse)]
+ * [same first page, "Integration": is_causal]
+ *
+ * Layout: q, k, v and o are contiguous row-major [B][H][N][d]; lse is
+ * contiguous [B][H][N] fp32. All five pointers are DEVICE pointers on the
+ * current HIP device. The caller allocates and frees every buffer; the
+ * library allocates nothing, frees nothing, keeps no state between calls and
+ * does not synchronize.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL means the
+ * default stream) and the call returns once it is launched. Results are
+ * valid after the caller synchronizes that stream. Faults during execution
+ * surface at that synchronization, not as a return code.
+ *
+ * Errors: every argument check runs before anything is launched; a non-zero
+ * status means nothing was enqueued (FA_ERR_LAUNCH: the launch itself was
+ * rejected by the runtime). B*H*N == 0 is a valid empty call: it returns
+ * FA_OK at once and the pointers are not looked at.
+ */
+#ifndef IO_AWARE_TILED_09_FA_H
+#define IO_AWARE_TILED_09_FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL_PTR = 1,            /* a pointer is NULL in a non-empty call      */
+    FA_ERR_BAD_SHAPE = 2,           /* B, H or N negative                          */
+    FA_ERR_UNSUPPORTED_HEAD_DIM = 3,/* d is not 64 or 128                          */
+    FA_ERR_BAD_SCALE = 4,           /* scale negative, NaN or infinite             */
+    FA_ERR_MISALIGNED = 5,          /* q/k/v/o not 16-byte aligned, lse not 4-byte */
+    FA_ERR_ALIASING = 6,            /* o or lse overlaps q, k, v or each other     */
+    FA_ERR_LAUNCH = 7,              /* the HIP runtime rejected the launch         */
+    FA_ERR_TOO_LARGE = 8            /* B*H*ceil(N/128) workgroups exceed 2^31 - 1  */
+} fa_status;
+
+/*
+ * bf16 attention forward.
+ * q, k, v: const bf16 (raw 16-bit bfloat16 bits) [B][H][N][d];
+ * o: bf16 [B][H][N][d], written with round-to-nearest-even;
+ * lse: fp32 [B][H][N], natural log;
+ * B, H, N >= 0; d in {64, 128}; scale >= 0 and finite (1/sqrt(d) is usual);
+ * causal: 0 or non-zero; stream: hipStream_t or NULL.
+ * Scores are accumulated in fp32 from exact bf16 products; softmax runs in
+ * fp32; P is rounded to bf16 before the P V product, which accumulates in fp32.
+ * Returns an fa_status.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int N, int d, float scale, int causal, void *stream);
+
+/*
+ * fp32-storage attention forward: q, k, v and o are fp32 [B][H][N][d]; every
+ * other argument as in fa_fwd. q, k and v are rounded to bf16 (nearest even)
+ * on load and take the same bf16 matrix-core path; o is stored in fp32.
+ */
+int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
+               float *lse, int B, int H, int N, int d, float scale, int causal,
+               void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *fa_status_string(int status);
+
+/* Queries per workgroup tile (Br) and keys per K/V tile (Bc) the kernels
+ * use; informational, for grid-size arithmetic in callers and tests. */
+int fa_tile_rows(void);
+int fa_tile_cols(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IO_AWARE_TILED_09_FA_H */

@@ -1,0 +1,128 @@
+"""ctypes binding of libfa.so: argument marshalling only.
+
+Every step of the forward pass runs in the HIP kernels behind the C ABI in
+include/fa.h. This module passes device pointers, sizes and the stream
+handle through, and there is no other implementation to fall back to: when
+libfa.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+_lib = None
+
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEAD_DIM",
+    4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_MISALIGNED", 6: "FA_ERR_ALIASING", 7: "FA_ERR_LAUNCH",
+    8: "FA_ERR_TOO_LARGE",
+}
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_status_string", "fa_tile_rows", "fa_tile_cols")
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {fa_status_string(status)}")
+
+
+def load():
+    """Load libfa.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    for name in ("fa_fwd", "fa_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        fn.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_tile_rows.restype = i
+    lib.fa_tile_cols.restype = i
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    return x.data_ptr() or None
+
+
+def _stream(stream, tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    for t in tensors:
+        if hasattr(t, "is_cuda") and t.is_cuda:
+            import torch
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
+    """C fa_fwd: bf16 q, k, v, o [B,H,N,d] and fp32 lse [B,H,N] device tensors
+    (or raw device addresses). stream: a torch stream, a raw hipStream_t int,
+    or None for the current torch stream of the tensors' device. Returns the
+    fa_status code."""
+    return int(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                             int(N), int(d), float(scale), int(bool(causal)),
+                             _stream(stream, (q, k, v, o, lse))))
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
+    """C fa_fwd_f32: as fa_fwd with fp32 q, k, v and o."""
+    return int(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
+                                 int(H), int(N), int(d), float(scale), int(bool(causal)),
+                                 _stream(stream, (q, k, v, o, lse))))
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_tile_rows() -> int:
+    return int(load().fa_tile_rows())
+
+
+def fa_tile_cols() -> int:
+    return int(load().fa_tile_cols())
+
+
+def attention(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """Allocate o and lse with torch (when not given) and run the forward pass.
+
+    q, k, v: contiguous [B, H, N, d] CUDA tensors, all bf16 or all fp32.
+    scale defaults to 1/sqrt(d). Returns (o, lse); raises FAError on a status.
+    """
+    import torch
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bf16 or all fp32")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    st = fn(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return out, lse

@@ -1,0 +1,106 @@
+// C ABI of the attention-forward library: argument checks, then one kernel
+// launch on the caller's stream. See include/fa.h for the contract.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_fwd_kernel.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;  // log2(e)
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks shared by both entry points. Returns FA_OK when a launch may follow;
+// *empty is set when the call has nothing to do.
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             int B, int H, int N, int d, float scale, size_t elem, bool* empty)
+{
+    *empty = false;
+    if (B < 0 || H < 0 || N < 0)
+        return FA_ERR_BAD_SHAPE;
+    if (B == 0 || H == 0 || N == 0) {
+        *empty = true;
+        return FA_OK;
+    }
+    if (!q || !k || !v || !o || !lse)
+        return FA_ERR_NULL_PTR;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!isfinite(scale) || scale < 0.0f)
+        return FA_ERR_BAD_SCALE;
+    const long long nqb = ((long long)N + fa::kBr - 1) / fa::kBr;
+    if ((long long)B * H * nqb > 0x7fffffffLL)
+        return FA_ERR_TOO_LARGE;
+    auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
+    if ((addr(q) | addr(k) | addr(v) | addr(o)) & 15u)
+        return FA_ERR_MISALIGNED;
+    if (addr(lse) & 3u)
+        return FA_ERR_MISALIGNED;
+    const uintptr_t tensor_bytes = (uintptr_t)B * (uintptr_t)H * (uintptr_t)N * (uintptr_t)d * elem;
+    const uintptr_t lse_bytes = (uintptr_t)B * (uintptr_t)H * (uintptr_t)N * sizeof(float);
+    const Range rq{addr(q), addr(q) + tensor_bytes}, rk{addr(k), addr(k) + tensor_bytes},
+        rv{addr(v), addr(v) + tensor_bytes}, ro{addr(o), addr(o) + tensor_bytes},
+        rl{addr(lse), addr(lse) + lse_bytes};
+    if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv) || overlaps(ro, rl) ||
+        overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv))
+        return FA_ERR_ALIASING;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, void* stream)
+{
+    bool empty;
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, 2, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    const float scale_log2 = (float)((double)scale * kLog2e);
+    const hipError_t e = fa::launch_bf16(q, k, v, o, lse, B * H, N, d, scale_log2, causal != 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+               int H, int N, int d, float scale, int causal, void* stream)
+{
+    bool empty;
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, 4, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    const float scale_log2 = (float)((double)scale * kLog2e);
+    const hipError_t e = fa::launch_f32(q, k, v, o, lse, B * H, N, d, scale_log2, causal != 0,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+const char* fa_status_string(int status)
+{
+    switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL_PTR: return "a tensor pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "B, H and N must be >= 0";
+    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_BAD_SCALE: return "scale must be finite and >= 0";
+    case FA_ERR_MISALIGNED: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIASING: return "o or lse overlaps an input or each other";
+    case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    case FA_ERR_TOO_LARGE: return "too many workgroups (B*H*ceil(N/128) >= 2^31)";
+    default: return "unknown status";
+    }
+}
+
+int fa_tile_rows(void) { return fa::kBr; }
+int fa_tile_cols(void) { return fa::kBc; }
+
+}  // extern "C"

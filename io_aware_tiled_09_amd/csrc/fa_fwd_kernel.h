@@ -1,0 +1,19 @@
+// Internal interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+constexpr int kWaves = 4;            // wave64s per workgroup
+constexpr int kBr = kWaves * 32;     // query rows per workgroup (32 per wave)
+constexpr int kBc = 64;              // keys per K/V tile
+
+// Enqueue one forward pass on `stream`. Shapes are assumed validated:
+// BH = B*H >= 1, N >= 1, d in {64, 128}, BH*ceil(N/kBr) < 2^31.
+// scale_log2 = softmax scale * log2(e).
+hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int BH, int N, int d, float scale_log2, bool causal, hipStream_t stream);
+hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                      int BH, int N, int d, float scale_log2, bool causal, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,82 @@
+"""The C ABI seen from the host (CPU only: nothing here launches a kernel).
+
+Every call below fails an argument check, which the library performs before
+it touches the HIP runtime, or is an empty call that returns at once.
+"""
+import os
+import re
+
+import pytest
+
+import io_aware_tiled_09_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+A = 0x7F0000000000  # a fake, 16-byte aligned device address (never dereferenced)
+MB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    names = _declared_functions()
+    assert set(names) == set(fa.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert fa.fa_status_string(0) == "ok"
+    for code in range(1, 9):
+        s = fa.fa_status_string(code)
+        assert s and s != "unknown status"
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+def test_tile_shape():
+    assert fa.fa_tile_rows() == 128 and fa.fa_tile_cols() == 64
+
+
+def _call(fn=fa.fa_fwd, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+          B=1, H=2, N=100, d=64, scale=0.125, causal=0):
+    return fn(q, k, v, o, lse, B, H, N, d, scale, causal, 0)
+
+
+@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+def test_argument_errors(fn):
+    assert _call(fn, q=0) == 1
+    assert _call(fn, lse=0) == 1
+    assert _call(fn, B=-1) == 2
+    assert _call(fn, N=-5) == 2
+    assert _call(fn, d=96) == 3
+    assert _call(fn, d=256) == 3
+    assert _call(fn, scale=float("nan")) == 4
+    assert _call(fn, scale=float("inf")) == 4
+    assert _call(fn, scale=-0.5) == 4
+    assert _call(fn, q=A + 8) == 5
+    assert _call(fn, o=A + 192 * MB + 4) == 5
+    assert _call(fn, lse=A + 256 * MB + 2) == 5
+    assert _call(fn, o=A) == 6                       # o is q
+    assert _call(fn, lse=A + 64 * MB + 1024) == 6    # lse inside k
+    assert _call(fn, lse=A + 192 * MB + 128) == 6    # lse inside o
+    assert _call(fn, B=65536, H=65536, N=128) == 8   # 2^32 workgroups
+
+
+@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+def test_empty_calls_return_ok_without_pointers(fn):
+    for B, H, N in ((0, 4, 100), (2, 0, 100), (2, 4, 0)):
+        assert fn(None, None, None, None, None, B, H, N, 64, 0.125, 1, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from io_aware_tiled_09_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "libfa.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.fa_fwd(A, A, A, A, A, 1, 1, 1, 64, 1.0, 0)

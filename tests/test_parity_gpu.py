@@ -1,0 +1,159 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs are the seeded generators' tensors; the oracle receives the exact
+values the GPU receives (bf16 or fp32, upcast to fp64). Bounds are in
+tests/_parity.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_09_amd as fa
+import oracle
+from io_aware_tiled_09_amd.inputs import WORKLOADS, make_qkv, sample_rows
+
+from _parity import assert_close, check_full, check_rows, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+TINY_N = [1, 2, 3, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 257]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", TINY_N)
+def test_tiny_shapes(N, d, causal):
+    say(f"tiny N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B=1, H=2, N=N, d=d, seed=N * 7 + d)
+    check_full(q, k, v, causal, 1.0 / math.sqrt(d), f"N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_multi_tile(d, causal):
+    say(f"ragged B=2 H=3 N=333 d={d} causal={causal}")
+    q, k, v = make_qkv(B=2, H=3, N=333, d=d, seed=11 + d)
+    check_full(q, k, v, causal, 1.0 / math.sqrt(d), "N=333")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_storage_path(d):
+    say(f"fp32 storage B=2 H=2 N=300 d={d}")
+    for causal in (False, True):
+        q, k, v = make_qkv(B=2, H=2, N=300, d=d, dtype="fp32", seed=21 + d)
+        check_full(q, k, v, causal, 1.0 / math.sqrt(d), f"fp32 causal={causal}")
+
+
+@pytest.mark.parametrize("name", ["single_head", "bert512", "gpt2_1k", "gpt2_1k_spiky"])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    say(f"workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} {w.dtype}")
+    q, k, v = make_qkv(w)
+    check_full(q, k, v, w.causal, w.scale, name)
+
+
+def _rows_for(w, count):
+    rows = sample_rows(w.N, count, seed=w.seed + 77, heads=w.B * w.H)
+    fixed = torch.tensor([31, 32, 63, 64, 127, 128, 129, w.N // 2, w.N - 2, w.N - 1],
+                         dtype=torch.int64)
+    return torch.cat([rows, fixed.expand(w.B * w.H, -1)], dim=1)
+
+
+@pytest.mark.parametrize("name,count", [("longdoc8k", 48), ("longctx32k", 256)])
+def test_workload_sampled_rows(name, count):
+    w = WORKLOADS[name]
+    count = w.oracle_rows or count
+    say(f"workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}, "
+        f"{count}+10 rows per head")
+    q, k, v = make_qkv(w)
+    check_rows(q, k, v, w.causal, w.scale, _rows_for(w, count), name)
+
+
+def test_deterministic_bitwise():
+    say("determinism B=2 H=4 N=1000 d=128 causal")
+    q, k, v = (t.cuda() for t in make_qkv(B=2, H=4, N=1000, d=128, seed=5))
+    o1, l1 = fa.attention(q, k, v, causal=True)
+    o2, l2 = fa.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_no_writes_outside_outputs(dtype):
+    say(f"canaries {dtype}")
+    B, H, N, d = 1, 3, 77, 64
+    q, k, v = (t.cuda() for t in make_qkv(B=B, H=H, N=N, d=d, seed=9,
+                                          dtype="bf16" if dtype == torch.bfloat16 else "fp32"))
+    pad = 4096
+    n = B * H * N * d
+    obuf = torch.full((pad + n + pad,), 7.0, dtype=dtype, device="cuda")
+    lbuf = torch.full((pad + B * H * N + pad,), 7.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + n].view(B, H, N, d)
+    lse = lbuf[pad:pad + B * H * N].view(B, H, N)
+    fa.attention(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert (obuf[:pad] == 7.0).all() and (obuf[pad + n:] == 7.0).all()
+    assert (lbuf[:pad] == 7.0).all() and (lbuf[pad + B * H * N:] == 7.0).all()
+    o_ref, lse_ref = oracle.attention_fwd(q.cpu(), k.cpu(), v.cpu(), 1 / 8, True)
+    assert_close(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, lse_ref, "canary")
+
+
+def test_side_stream():
+    say("non-default stream")
+    q, k, v = (t.cuda() for t in make_qkv(B=1, H=4, N=700, d=128, seed=3))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, lse = fa.attention(q, k, v, causal=True)
+    s.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(q.cpu(), k.cpu(), v.cpu(), 1 / math.sqrt(128), True)
+    assert_close(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, lse_ref, "stream")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_zero_gives_means(causal):
+    say(f"scale 0 causal={causal}")
+    B, H, N, d = 1, 2, 190, 64
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=4)
+    o, lse = run_gpu(q, k, v, causal, 0.0)
+    vv = v.double()
+    if causal:
+        ref = torch.cumsum(vv, dim=2) / torch.arange(1, N + 1, dtype=torch.float64).view(1, 1, N, 1)
+        lref = torch.log(torch.arange(1, N + 1, dtype=torch.float64)).expand(B, H, N)
+    else:
+        ref = vv.mean(dim=2, keepdim=True).expand_as(vv)
+        lref = torch.full((B, H, N), math.log(N), dtype=torch.float64)
+    assert_close(o.numpy(), lse.numpy(), ref.numpy(), lref.numpy(), "scale=0")
+
+
+def test_large_logits_d128():
+    say("large logits: q, k x8 at d=128")
+    q, k, v = make_qkv(B=1, H=2, N=520, d=128, seed=8)
+    q = (q.float() * 8).to(torch.bfloat16)
+    k = (k.float() * 8).to(torch.bfloat16)
+    check_full(q, k, v, True, 1 / math.sqrt(128), "x8 logits")
+
+
+def test_gpu_argument_errors():
+    say("argument errors on device tensors")
+    q, k, v = (t.cuda() for t in make_qkv(B=1, H=1, N=64, d=64, seed=1))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, 64), device="cuda")
+    flat = torch.empty(64 * 64 + 8, dtype=torch.bfloat16, device="cuda")
+    mis = flat[1:1 + 64 * 64].view(1, 1, 64, 64)
+    assert fa.fa_fwd(mis, k, v, o, lse, 1, 1, 64, 64, 0.125, 0) == 5
+    assert fa.fa_fwd(q, k, v, q, lse, 1, 1, 64, 64, 0.125, 0) == 6
+    with pytest.raises(fa.FAError):
+        fa.attention(q[..., :32].contiguous(), k[..., :32].contiguous(), v[..., :32].contiguous())
+    torch.cuda.synchronize()
+
+
+def test_empty_sequence():
+    say("empty N=0")
+    q = torch.empty((2, 3, 0, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = fa.attention(q, q, q, causal=True)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 64) and lse.shape == (2, 3, 0)
