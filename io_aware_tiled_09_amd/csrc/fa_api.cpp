@@ -5,7 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/fa.h"
-#include "fa_fwd_kernel.h"
+#include "fa_kernels.h"
 
 namespace {
 

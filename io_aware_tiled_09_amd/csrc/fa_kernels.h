@@ -10,7 +10,7 @@ constexpr int kBc = 64;              // keys per K/V tile
 
 // Enqueue one forward pass on `stream`. Shapes are assumed validated:
 // BH = B*H >= 1, N >= 1, d in {64, 128}, BH*ceil(N/kBr) < 2^31.
-// scale_log2 = softmax scale * log2(e).
+// scale_log2 = softmax scale * log2(e) >= 0.
 hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                        int BH, int N, int d, float scale_log2, bool causal, hipStream_t stream);
 hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, float* lse,
