@@ -1,6 +1,7 @@
 // C ABI of the attention-forward library: argument checks, then one kernel
 // launch on the caller's stream. See include/fa.h for the contract.
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -54,6 +55,16 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
     return FA_OK;
 }
 
+// The kernels take scale*log2(e) and need it > 0, so that a masked score
+// (-inf) always gives exp2(-inf) = 0. Raising a smaller value to FLT_MIN
+// changes nothing: with scale*log2(e) <= FLT_MIN every exponent of a visible
+// key rounds to 0 in fp32, exactly as with scale 0 (all weights 1).
+float kernel_scale(float scale)
+{
+    const float c = (float)((double)scale * kLog2e);
+    return c < FLT_MIN ? FLT_MIN : c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -65,7 +76,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     const int st = validate(q, k, v, o, lse, B, H, N, d, scale, 2, &empty);
     if (st != FA_OK || empty)
         return st;
-    const float scale_log2 = (float)((double)scale * kLog2e);
+    const float scale_log2 = kernel_scale(scale);
     const hipError_t e = fa::launch_bf16(q, k, v, o, lse, B * H, N, d, scale_log2, causal != 0,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -78,7 +89,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
     const int st = validate(q, k, v, o, lse, B, H, N, d, scale, 4, &empty);
     if (st != FA_OK || empty)
         return st;
-    const float scale_log2 = (float)((double)scale * kLog2e);
+    const float scale_log2 = kernel_scale(scale);
     const hipError_t e = fa::launch_f32(q, k, v, o, lse, B * H, N, d, scale_log2, causal != 0,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_common.h"
 
 namespace fa {
@@ -100,8 +102,11 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                         float* __restrict__ lse, int BH, int N, int nqb, float scale_log2)
 {
     using TL = Tile<D>;
-    // [buffer][0 = K, 1 = V][tile bytes], swizzled rows
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TL::kBytes];
+    // K and V tiles, double-buffered each, rows swizzled. K runs one tile
+    // ahead of V: while the softmax of tile j runs, the scores of tile j+1
+    // are produced from K_{j+1}, and P_j meets V_j afterwards.
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TL::kBytes];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases in SGPRs
@@ -128,7 +133,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                        : bf16x8{};
     // Retire the Q loads here, visibly to the compiler's wait-count pass
     // (s_waitcnt vmcnt(0)); otherwise it keeps a vmcnt(0) inside the loop,
-    // which would also wait for the next tile's loads in flight.
+    // which would also wait for the next tiles' loads in flight.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // Direct loads: this wave's load `it` of a tile fills LDS bytes
@@ -143,28 +148,24 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         const int lchunk = (lane % TL::kChunks) ^ TL::swz(row);
         ld_off[it] = row * TL::kRowBytes + lchunk * 16;
     }
-    auto issue_tile = [&](int kb, int buf) {
+    auto issue = [&](const __bf16* src, int kb, unsigned char* dst) {
         const int j0 = kb * kBc;
         const unsigned bytes = (unsigned)min(kBc, N - j0) * TL::kRowBytes;
-        const i32x4 rk = buffer_rsrc(kh + (size_t)j0 * D, bytes);
-        const i32x4 rv = buffer_rsrc(vh + (size_t)j0 * D, bytes);
+        const i32x4 rs = buffer_rsrc(src + (size_t)j0 * D, bytes);
 #pragma unroll
-        for (int it = 0; it < TL::kLoadsPerWave; ++it) {
-            const int n = wave * TL::kLoadsPerWave + it;
-            lds_dma16(rk, ld_off[it], lds_addr(&smem[buf][0][n * 1024]));
-            lds_dma16(rv, ld_off[it], lds_addr(&smem[buf][1][n * 1024]));
-        }
+        for (int it = 0; it < TL::kLoadsPerWave; ++it)
+            lds_dma16(rs, ld_off[it], lds_addr(dst + (wave * TL::kLoadsPerWave + it) * 1024));
     };
-    // Rows of a partial last tile past the sequence end: V must hold finite
-    // values there (their probabilities are 0, and 0 * NaN would leak), so
-    // they are cleared once the tile's loads have landed.
-    auto clear_tail = [&](int kb, int buf) {
+    // Rows of a partial last V tile past the sequence end must hold finite
+    // values (their probabilities are 0, and 0 * NaN would leak), so they are
+    // cleared once the tile's loads have landed. Partial K rows need nothing:
+    // their scores are replaced by -inf.
+    auto clear_tail = [&](int kb, unsigned char* dst) {
         const int rows = N - kb * kBc;
         if (rows >= kBc) return;
         for (int x = tid; x < (kBc - rows) * TL::kChunks; x += kThreads) {
             const int row = rows + x / TL::kChunks;
-            *reinterpret_cast<bf16x8*>(&smem[buf][1][row * TL::kRowBytes + (x % TL::kChunks) * 16]) =
-                bf16x8{};
+            *reinterpret_cast<bf16x8*>(dst + row * TL::kRowBytes + (x % TL::kChunks) * 16) = bf16x8{};
         }
     };
 
@@ -187,8 +188,39 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             v_off[tt][s] = key * TL::kRowBytes + (((d0 / 8) ^ TL::swz(key)) * 16) + (d0 % 8) * 2;
         }
 
+    // S^T tile of 64 keys from the K tile at kt.
+    auto scores = [&](const unsigned char* kt, f32x16 (&s)[kBc / 32]) {
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) {
+            s[st] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + st * 32 * TL::kRowBytes + k_off[c]);
+                s[st] = mfma(kf, qf[c], s[st]);
+            }
+        }
+    };
+    // Replace the scores of invisible keys (past N, or after the query when
+    // causal) by -inf.
+    auto mask = [&](int kb, f32x16 (&s)[kBc / 32]) {
+        const int j0 = kb * kBc;
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = j0 + score_key(st, r, lh);
+                const bool ok = j < N && (!CAUSAL || j <= qi);
+                s[st][r] = ok ? s[st][r] : neg_inf();
+            }
+    };
+    // A wave whose 32 rows all precede a tile's first key skips that tile.
+    auto active = [&](int kb) { return !CAUSAL || kb * kBc <= qw0 + 31; };
+
     const int nkb_all = (N + kBc - 1) / kBc;
-    const int kb_end = CAUSAL ? min(nkb_all, (q0 + kBr - 1) / kBc + 1) : nkb_all;
+    const int nkb = CAUSAL ? min(nkb_all, (q0 + kBr - 1) / kBc + 1) : nkb_all;
+    // Tiles [0, nfull) need no mask for any wave of the workgroup: all their
+    // keys are < N and (causal) <= the workgroup's first query q0.
+    const int nfull = min(CAUSAL ? (q0 + 1) / kBc : nkb_all, N / kBc);
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -196,74 +228,66 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     float m_run = neg_inf();  // running max, base-2 scaled domain
     float l_run = 0.f;        // this lane's share of the running sum
 
-    issue_tile(0, 0);
+    // ---- prologue: K_0, V_0 (and K_1) in LDS; scores of tile 0
+    issue(kh, 0, kbuf[0]);
+    issue(vh, 0, vbuf[0]);
+    if (nkb > 1) issue(kh, 1, kbuf[1]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    clear_tail(0, 0);
+    clear_tail(0, vbuf[0]);
     __syncthreads();
+    f32x16 s_cur[kBc / 32];
+    scores(kbuf[0], s_cur);
+    __syncthreads();  // kbuf[0] is free for K_2
 
-    for (int kb = 0; kb < kb_end; ++kb) {
-        const int buf = kb & 1;
-        const int j0 = kb * kBc;
-        if (kb + 1 < kb_end) issue_tile(kb + 1, buf ^ 1);
+    // One key tile: softmax of tile kb (its scores are in s_cur) and, in the
+    // same block so that they overlap, the scores of tile kb+1; then
+    // O^T = alpha * O^T + V^T P^T. MASKED tiles first replace invisible
+    // scores by -inf (a compile-time choice: the interior loop carries no
+    // mask code at all).
+    auto tile = [&](auto masked, int kb) {
+        constexpr bool MASKED = decltype(masked)::value;
+        // In LDS now: K_{kb+1} in kbuf[(kb+1)&1], V_kb in vbuf[kb&1].
+        if (kb + 2 < nkb) issue(kh, kb + 2, kbuf[kb & 1]);
+        if (kb + 1 < nkb) issue(vh, kb + 1, vbuf[(kb + 1) & 1]);
+        const bool has_next = kb + 1 < nkb && active(kb + 1);
+        f32x16 s_next[kBc / 32];
 
-        // A wave whose 32 rows all precede this tile's first key has nothing to do.
-        if (!CAUSAL || j0 <= qw0 + 31) {
-            const unsigned char* kt = smem[buf][0];
-            const unsigned char* vt = smem[buf][1];
-
-            // ---- S^T = K Q^T: two 32-key sub-tiles
-            f32x16 s[kBc / 32];
-#pragma unroll
-            for (int st = 0; st < kBc / 32; ++st) {
-                bf16x8 kf[D / 16];
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c)
-                    kf[c] = *reinterpret_cast<const bf16x8*>(kt + st * 32 * TL::kRowBytes + k_off[c]);
-                s[st] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c) s[st] = mfma(kf[c], qf[c], s[st]);
-            }
-
-            // ---- mask where needed; tile row max on the raw scores
-            const bool need_mask = (j0 + kBc > N) || (CAUSAL && j0 + kBc - 1 > qw0);
-            if (need_mask) {
+        if (active(kb)) {
+            if constexpr (MASKED) mask(kb, s_cur);
+            bool grow;
+            float alpha;
+            bf16x8 pf[1][kBc / 32][2];
+            auto softmax = [&]() {
+                float mraw = neg_inf();
 #pragma unroll
                 for (int st = 0; st < kBc / 32; ++st)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int j = j0 + score_key(st, r, lh);
-                        const bool ok = j < N && (!CAUSAL || j <= qi);
-                        s[st][r] = ok ? s[st][r] : neg_inf();
-                    }
-            }
-            float mraw = neg_inf();
-#pragma unroll
-            for (int st = 0; st < kBc / 32; ++st)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[st][r]);
-            mraw = max_with_partner(mraw);
-            // scale >= 0, so the scaled max is scale_log2 * raw max
-            const float mtile = mraw > neg_inf() ? mraw * scale_log2 : neg_inf();
-
-            // ---- new running max; rescale only if some row's max grew
-            const bool grow = mtile > m_run;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
+                    for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s_cur[st][r]);
+                mraw = max_with_partner(mraw);
+                // scale >= 0, so the scaled max is scale_log2 * raw max
+                const float mtile = mraw > neg_inf() ? mraw * scale_log2 : neg_inf();
+                grow = mtile > m_run;
                 const float m_new = grow ? mtile : m_run;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                 m_run = m_new;
-                l_run *= alpha;
+                const float lsum = probs<false, 1>(s_cur, scale_log2, m_run, pf);
+                l_run = l_run * alpha + lsum;
+            };
+            if (has_next) {
+                softmax();
+                scores(kbuf[(kb + 1) & 1], s_next);
+            } else {
+                softmax();
+            }
+
+            // alpha == 1 unless some row's max grew
+            if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
                 for (int t = 0; t < D / 32; ++t)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
             }
-
-            // ---- probabilities, row sum, bf16 P fragments
-            bf16x8 pf[1][kBc / 32][2];
-            l_run += need_mask ? probs<true, 1>(s, scale_log2, m_run, pf)
-                               : probs<false, 1>(s, scale_log2, m_run, pf);
-
-            // ---- O^T += V^T P^T
+            const unsigned char* vt = vbuf[kb & 1];
 #pragma unroll
             for (int tt = 0; tt < D / 32; ++tt) {
 #pragma unroll
@@ -283,10 +307,16 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             }
         }
 
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of the next tile
-        if (kb + 1 < kb_end) clear_tail(kb + 1, buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of the next tiles
+        if (kb + 1 < nkb) clear_tail(kb + 1, vbuf[(kb + 1) & 1]);
         __syncthreads();
-    }
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) s_cur[st] = s_next[st];
+    };
+
+    int kb = 0;
+    for (; kb < nfull; ++kb) tile(std::false_type{}, kb);
+    for (; kb < nkb; ++kb) tile(std::true_type{}, kb);
 
     // ---- epilogue: O = acc / l, lse = (m2 + log2 l) * ln 2
     const float l_tot = sum_with_partner(l_run);
