@@ -59,6 +59,54 @@ def measured_traffic(digest: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def _counter_means(path, counter):
+    import csv
+    by_kernel = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                by_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k_: sum(v_) / len(v_) for k_, v_ in by_kernel.items()}
+
+
+def ingest_counters(fetch_csv, write_csv, copy_mib, command):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch) of `command` into HBM bytes per attention launch, each counter
+    scaled by what it reads for the plain device copy of copy_mib MiB that the
+    same command runs (its true traffic is copy_mib MiB read + written)."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+
+    def pick(table, needle):
+        hits = [v_ for k_, v_ in table.items() if needle in k_]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {needle!r}, found {len(hits)}")
+        return hits[0]
+
+    attn = "fa_fwd_bf16_kernel"
+    copy = "copyBuffer"
+    true_kib = copy_mib * 1024.0
+    f_fetch = true_kib / pick(fetch, copy)
+    f_write = true_kib / pick(write, copy)
+    fetch_kib, write_kib = pick(fetch, attn), pick(write, attn)
+    traffic = (fetch_kib * f_fetch + write_kib * f_write) * 1024.0
+    out = {
+        "kernel_source_digest": kernel_source_digest(),
+        "workload": "longdoc8k",
+        "hbm_bytes_per_launch": round(traffic),
+        "fetch_kib_raw": fetch_kib,
+        "write_kib_raw": write_kib,
+        "copy_kib_true": true_kib,
+        "fetch_scale": f_fetch,
+        "write_scale": f_write,
+        "command": command,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
     """Time the oracle over whole heads of the workload until about budget_s."""
     import oracle
@@ -97,7 +145,15 @@ def main(argv=None):
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB 3 times "
                          "(reference kernel for HBM counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: write the HBM traffic summary from two rocprofv3 "
+                         "counter CSVs of a run made with --copy-kernel-mib")
+    ap.add_argument("--profile-command", default="",
+                    help="with --ingest-counters: the command line the counters came from")
     args = ap.parse_args(argv)
+    if args.ingest_counters:
+        return ingest_counters(*args.ingest_counters, args.copy_kernel_mib or 1024,
+                               args.profile_command)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this attention forward has no "
