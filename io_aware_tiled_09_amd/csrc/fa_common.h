@@ -78,20 +78,24 @@ __device__ inline float probs(const f32x16 (&s)[kBc / 32], float c, float m,
     return lsum;
 }
 
-// Work split over (batch*head, query block): causal blocks heaviest first
-// (largest query-block index), heads fastest, so that early waves of the
-// grid carry the long rows and the short ones fill the tail.
+// Work split over (batch*head, query block).
 // [FlashAttention: The GPU Memory Hack That Changed Everything,
 //  "FlashAttention-2": parallelism over the sequence dimension]
+// Consecutive workgroup ids go round-robin to the 8 XCDs, each with its own
+// L2. When the grid divides evenly, XCD x gets one contiguous run of the
+// (head, query block) sequence, so the query blocks of a head run side by
+// side on one XCD and read the same K/V tiles through the same L2. Within a
+// head, causal blocks go heaviest first (largest query-block index), so each
+// XCD's stream ends with short blocks.
+constexpr int kXcds = 8;
+
 template <bool CAUSAL>
 __device__ inline void block_coords(int L, int BH, int nqb, int& qb, int& bh) {
-    if (CAUSAL) {
-        qb = nqb - 1 - L / BH;
-        bh = L % BH;
-    } else {
-        qb = L % nqb;
-        bh = L / nqb;
-    }
+    const int total = BH * nqb;
+    const int idx = total % kXcds == 0 ? (L % kXcds) * (total / kXcds) + L / kXcds : L;
+    bh = idx / nqb;
+    const int r = idx - bh * nqb;
+    qb = CAUSAL ? nqb - 1 - r : r;
 }
 
 }  // namespace fa
