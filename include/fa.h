@@ -67,8 +67,10 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 
 /*
  * fp32-storage attention forward: q, k, v and o are fp32 [B][H][N][d]; every
- * other argument as in fa_fwd. q, k and v are rounded to bf16 (nearest even)
- * on load and take the same bf16 matrix-core path; o is stored in fp32.
+ * other argument as in fa_fwd. Each fp32 operand x is split into two bf16
+ * terms, hi = rn(x) and lo = rn(x - hi), and every product is taken as
+ * hi*hi + lo*hi + hi*lo on the bf16 matrix cores with fp32 accumulation, so
+ * scores and P V keep close to fp32 accuracy; o is stored in fp32.
  */
 int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
                float *lse, int B, int H, int N, int d, float scale, int causal,
@@ -77,8 +79,9 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_string(int status);
 
-/* Queries per workgroup tile (Br) and keys per K/V tile (Bc) the kernels
- * use; informational, for grid-size arithmetic in callers and tests. */
+/* Queries per workgroup tile (Br) of the bf16 kernel (fa_fwd; fa_fwd_f32
+ * uses 128) and keys per K/V tile (Bc) of both kernels; informational, for
+ * grid-size arithmetic in callers and tests. */
 int fa_tile_rows(void);
 int fa_tile_cols(void);
 

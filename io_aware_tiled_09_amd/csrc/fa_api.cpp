@@ -111,7 +111,7 @@ const char* fa_status_string(int status)
     }
 }
 
-int fa_tile_rows(void) { return fa::kBr; }
+int fa_tile_rows(void) { return fa::kBrBf16; }
 int fa_tile_cols(void) { return fa::kBc; }
 
 }  // extern "C"

@@ -10,7 +10,18 @@
 // "FlashAttention-2" section (parallelism over the sequence).
 //
 // gfx950 mapping (this file's own design):
-//  * One workgroup = 4 wave64s = 128 query rows; each wave owns 32 rows.
+//  * One workgroup = 8 wave64s = 256 query rows; each wave owns 32 rows. The
+//    hardware places waves w and w+4 on the same SIMD (measured: every
+//    workgroup, every CU), so group 0 = waves 0-3 and group 1 = waves 4-7
+//    put one wave of each group on every SIMD.
+//  * Per key tile j a wave runs two phases: A(j) = the softmax of tile j
+//    (row max, exp2, row sum, bf16 P, output rescale: VALU and
+//    transcendental work only) and B(j) = the scores of tile j+1 and
+//    O += P_j V_j (32 MFMAs and their LDS reads, no other work). Group 1
+//    runs one phase behind group 0 and every phase ends with a workgroup
+//    barrier, so on each SIMD one wave feeds the matrix core while the other
+//    runs the softmax: the two kinds of work overlap by construction instead
+//    of by chance. Scheduling fences keep each instruction inside its phase.
 //  * Scores are produced transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
 //    A = K tile from LDS (32 keys x 16 of d), B = the wave's Q fragment held
 //    in VGPRs for the whole loop. In the 32x32 accumulator layout a lane
@@ -22,10 +33,14 @@
 //    column per lane) comes from two ds_read_b64_tr_b16 transpose reads: in
 //    each 16-lane group, lanes 4k..4k+3 point at 16 consecutive d values of
 //    key k and lane i receives d column i of the 4 keys.
-//  * K/V tiles (64 keys) go from HBM straight into LDS with
-//    buffer_load_dwordx4 ... lds (no VGPR staging), double-buffered: the next
-//    tile is in flight while the current one is consumed; one barrier per
-//    tile. Buffer-resource bounds make rows past the sequence end read as 0.
+//  * K and V tiles (64 keys) go from HBM straight into LDS with
+//    buffer_load_dwordx4 ... lds (no VGPR staging) through two rings of four
+//    tiles each (128 KiB at d = 128, one workgroup per CU). Every phase, each
+//    wave issues its share of one tile (V in even phases, K in odd ones),
+//    which has four phases (two tiles) to land before it is read. Ring slot
+//    and sub-tile offsets are instruction immediates: the loop is unrolled
+//    by the ring size. Buffer-resource bounds make rows past the sequence
+//    end read as 0.
 //  * LDS rows hold 16-byte chunks XOR-swizzled by row, so that the K reads
 //    (16 rows, same chunk) and the V transpose reads (4 rows x 4 chunks per
 //    32 lanes) hit distinct banks.
@@ -46,6 +61,17 @@
 namespace fa {
 namespace {
 
+constexpr int kPPWaves = 8;                  // two groups of four wave64s
+constexpr int kPPThreads = kPPWaves * 64;
+constexpr int kRing = 4;                     // K (and V) tiles resident in LDS
+// __builtin_amdgcn_sched_group_barrier instruction classes
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+// LDS reads issued ahead of the MFMA that consumes them, in MFMAs
+// (measured flat from 2 to 8; 6 leaves the register budget unspilled).
+constexpr int kReadAhead = 6;
+static_assert(kBrBf16 == kPPWaves * 32, "32 query rows per wave");
+
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D>
@@ -54,8 +80,8 @@ struct Tile {
     static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
     static constexpr int kBytes = kBc * kRowBytes;          // one K or V tile
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;   // rows per wave-wide load
-    static constexpr int kLoadsPerWave = kBytes / 1024 / kWaves;
-    static_assert(kLoadsPerWave * 1024 * kWaves == kBytes, "tile must split over waves");
+    static constexpr int kLoadsPerWave = kBytes / 1024 / kPPWaves;
+    static_assert(kLoadsPerWave * 1024 * kPPWaves == kBytes, "tile must split over waves");
 
     // Physical 16-byte chunk slot of logical chunk c in tile row r is c ^ swz(r).
     // D = 128 (16 chunks/row, rows 256 B apart): a bijection of r mod 16 whose
@@ -71,8 +97,9 @@ struct Tile {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt unconstrained.
-constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate (gfx9 encoding) with only vmcnt constrained (n < 16):
+// expcnt and lgkmcnt keep their maximum values.
+constexpr int wait_vmcnt(int n) { return 0x0F70 | n; }
 
 // Raw buffer resource over [base, base + bytes): offsets past `bytes` read 0.
 __device__ inline i32x4 buffer_rsrc(const void* base, unsigned bytes) {
@@ -87,8 +114,8 @@ __device__ inline unsigned lds_addr(const void* p) {
 // One wave-wide load straight into LDS: lane i's 16 bytes at byte offset
 // `voff` of the buffer land at LDS address base + 16*i. Issued as inline asm
 // so that the compiler's wait-count pass does not treat later LDS reads of
-// the other buffer as dependent on it; the kernel waits for these loads
-// explicitly (vmcnt) before the barrier that publishes the tile. M0 carries
+// other ring slots as dependent on it; the kernel waits for these loads
+// explicitly (vmcnt) before the barrier that publishes a tile. M0 carries
 // the LDS base; the kernel uses M0 for nothing else.
 __device__ inline void lds_dma16(i32x4 rsrc, unsigned voff, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
@@ -96,20 +123,21 @@ __device__ inline void lds_dma16(i32x4 rsrc, unsigned voff, unsigned lds_base) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                         const __bf16* __restrict__ v, __bf16* __restrict__ o,
                         float* __restrict__ lse, int BH, int N, int nqb, float scale_log2)
 {
     using TL = Tile<D>;
-    // K and V tiles, double-buffered each, rows swizzled. K runs one tile
-    // ahead of V: while the softmax of tile j runs, the scores of tile j+1
-    // are produced from K_{j+1}, and P_j meets V_j afterwards.
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TL::kBytes];
+    constexpr int L = TL::kLoadsPerWave;
+    // Tile t of K lives in kring[t % 4], tile t of V in vring[t % 4]; rows
+    // are swizzled (Tile::swz).
+    __shared__ __attribute__((aligned(1024))) unsigned char kring[kRing][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vring[kRing][TL::kBytes];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases in SGPRs
+    const int grp = wave >> 2;  // waves w and w+4 share a SIMD
     const int lane = tid & 63;
     const int li = lane & 31;   // query column of this lane in the wave's 32
     const int lh = lane >> 5;   // which 8-element half of each 16-wide k slice
@@ -121,7 +149,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     const __bf16* kh = k + head_off;
     const __bf16* vh = v + head_off;
 
-    const int q0 = qb * kBr;
+    const int q0 = qb * kBrBf16;
     const int qw0 = q0 + wave * 32;   // first query of this wave
     const int qi = qw0 + li;          // this lane's query row
 
@@ -133,71 +161,93 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                        : bf16x8{};
     // Retire the Q loads here, visibly to the compiler's wait-count pass
     // (s_waitcnt vmcnt(0)); otherwise it keeps a vmcnt(0) inside the loop,
-    // which would also wait for the next tiles' loads in flight.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // which would also wait for the tile loads in flight.
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+
+    const int nkb_all = (N + kBc - 1) / kBc;
+    const int nkb = CAUSAL ? min(nkb_all, (q0 + kBrBf16 - 1) / kBc + 1) : nkb_all;
+    // Tiles [0, nfull) need no mask for any wave of the workgroup: all their
+    // keys are < N and (causal) <= the workgroup's first query q0.
+    const int nfull = min(CAUSAL ? (q0 + 1) / kBc : nkb_all, N / kBc);
+    // Last tile with a key visible to some row of this wave.
+    const int last = CAUSAL ? min(nkb - 1, (qw0 + 31) / kBc) : nkb - 1;
 
     // Direct loads: this wave's load `it` of a tile fills LDS bytes
-    // [n*1024, n*1024 + 1024), n = wave*kLoadsPerWave + it; lane i fills the
-    // 16-byte slot i there, i.e. row n*kRowsPerLoad + i / kChunks, physical
-    // chunk i % kChunks, which holds logical chunk (i % kChunks) ^ swz(row).
-    int ld_off[TL::kLoadsPerWave];
+    // [n*1024, n*1024 + 1024), n = wave*L + it; lane i fills the 16-byte slot
+    // i there, i.e. row n*kRowsPerLoad + i / kChunks, physical chunk
+    // i % kChunks, which holds logical chunk (i % kChunks) ^ swz(row).
+    int ld_off[L];
 #pragma unroll
-    for (int it = 0; it < TL::kLoadsPerWave; ++it) {
-        const int n = wave * TL::kLoadsPerWave + it;
+    for (int it = 0; it < L; ++it) {
+        const int n = wave * L + it;
         const int row = n * TL::kRowsPerLoad + lane / TL::kChunks;
         const int lchunk = (lane % TL::kChunks) ^ TL::swz(row);
         ld_off[it] = row * TL::kRowBytes + lchunk * 16;
     }
-    auto issue = [&](const __bf16* src, int kb, unsigned char* dst) {
-        const int j0 = kb * kBc;
-        const unsigned bytes = (unsigned)min(kBc, N - j0) * TL::kRowBytes;
-        const i32x4 rs = buffer_rsrc(src + (size_t)j0 * D, bytes);
+    // This wave's share of tile t of `src` into `dst`. A tile past the last
+    // one is still issued, with an empty buffer range (nothing is read), so
+    // that every wave issues exactly L loads per phase and the vmcnt
+    // arithmetic of the phase loop holds.
+    auto issue = [&](const __bf16* src, int t, unsigned char* dst) __attribute__((always_inline)) {
+        const int j0 = t * kBc;
+        const bool real = t < nkb;
+        const unsigned bytes = real ? (unsigned)min(kBc, N - j0) * TL::kRowBytes : 0u;
+        const i32x4 rs = buffer_rsrc(real ? src + (size_t)j0 * D : src, bytes);
 #pragma unroll
-        for (int it = 0; it < TL::kLoadsPerWave; ++it)
-            lds_dma16(rs, ld_off[it], lds_addr(dst + (wave * TL::kLoadsPerWave + it) * 1024));
+        for (int it = 0; it < L; ++it)
+            lds_dma16(rs, ld_off[it], lds_addr(dst + (wave * L + it) * 1024));
     };
     // Rows of a partial last V tile past the sequence end must hold finite
-    // values (their probabilities are 0, and 0 * NaN would leak), so they are
+    // values (their probabilities are 0, and 0 * NaN would leak); they are
     // cleared once the tile's loads have landed. Partial K rows need nothing:
     // their scores are replaced by -inf.
-    auto clear_tail = [&](int kb, unsigned char* dst) {
-        const int rows = N - kb * kBc;
+    auto clear_tail = [&](int t, unsigned char* dst) __attribute__((always_inline)) {
+        const int rows = N - t * kBc;
         if (rows >= kBc) return;
-        for (int x = tid; x < (kBc - rows) * TL::kChunks; x += kThreads) {
+        for (int x = tid; x < (kBc - rows) * TL::kChunks; x += kPPThreads) {
             const int row = rows + x / TL::kChunks;
             *reinterpret_cast<bf16x8*>(dst + row * TL::kRowBytes + (x % TL::kChunks) * 16) = bf16x8{};
         }
     };
 
+    // LDS byte addresses of the two rings, hidden from constant folding: all
+    // per-lane addresses below are ring base + lane offset in one VGPR, and
+    // the ring slot and sub-tile offsets (< 64 KiB from the ring base) ride in
+    // the instructions' 16-bit offset fields.
+    unsigned kbase = lds_addr(kring[0]), vbase = lds_addr(vring[0]);
+    asm volatile("" : "+s"(kbase), "+s"(vbase));
+
     // K fragment (A operand of S^T): key row st*32 + li, logical chunk 2c + lh.
-    int k_off[D / 16];
+    unsigned k_off[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-        k_off[c] = li * TL::kRowBytes + (((2 * c + lh) ^ TL::swz(li)) * 16);
+        k_off[c] = kbase + li * TL::kRowBytes + (((2 * c + lh) ^ TL::swz(li)) * 16);
 
     // V^T fragment (A operand of O^T += V^T P^T) by two transpose reads: for
     // read s (slots 4s..4s+3) lane l points at key 4*lh + (l % 16) / 4 + 8s of
     // the 16-key chunk and d = tt*32 + ((l / 16) % 2) * 16 + 4 * (l % 4).
-    int v_off[D / 32][2];
+    unsigned v_off[D / 32][2];
 #pragma unroll
     for (int tt = 0; tt < D / 32; ++tt)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int key = 4 * lh + (lane % 16) / 4 + 8 * s;
             const int d0 = tt * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
-            v_off[tt][s] = key * TL::kRowBytes + (((d0 / 8) ^ TL::swz(key)) * 16) + (d0 % 8) * 2;
+            v_off[tt][s] = vbase + key * TL::kRowBytes + (((d0 / 8) ^ TL::swz(key)) * 16) + (d0 % 8) * 2;
         }
 
-    // S^T tile of 64 keys from the K tile at kt.
-    auto scores = [&](const unsigned char* kt, f32x16 (&s)[kBc / 32]) {
+    // S^T tile of 64 keys from the K tile in ring slot `slot`: K fragment
+    // i = st * (D/16) + c is key row st*32 + li, d slice c*16 + lh*8.
+    constexpr int kKFrags = kBc / 32 * D / 16;
+    auto scores = [&](int slot, f32x16 (&s)[kBc / 32]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int st = 0; st < kBc / 32; ++st) {
-            s[st] = f32x16{};
+        for (int st = 0; st < kBc / 32; ++st) s[st] = f32x16{};
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + st * 32 * TL::kRowBytes + k_off[c]);
-                s[st] = mfma(kf, qf[c], s[st]);
-            }
+        for (int i = 0; i < kKFrags; ++i) {
+            const int st = i / (D / 16), c = i % (D / 16);
+            const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                (size_t)(k_off[c] + slot * TL::kBytes + st * 32 * TL::kRowBytes));
+            s[st] = mfma(kf, qf[c], s[st]);
         }
     };
     // Replace the scores of invisible keys (past N, or after the query when
@@ -213,14 +263,6 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                 s[st][r] = ok ? s[st][r] : neg_inf();
             }
     };
-    // A wave whose 32 rows all precede a tile's first key skips that tile.
-    auto active = [&](int kb) { return !CAUSAL || kb * kBc <= qw0 + 31; };
-
-    const int nkb_all = (N + kBc - 1) / kBc;
-    const int nkb = CAUSAL ? min(nkb_all, (q0 + kBr - 1) / kBc + 1) : nkb_all;
-    // Tiles [0, nfull) need no mask for any wave of the workgroup: all their
-    // keys are < N and (causal) <= the workgroup's first query q0.
-    const int nfull = min(CAUSAL ? (q0 + 1) / kBc : nkb_all, N / kBc);
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -228,95 +270,165 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     float m_run = neg_inf();  // running max, base-2 scaled domain
     float l_run = 0.f;        // this lane's share of the running sum
 
-    // ---- prologue: K_0, V_0 (and K_1) in LDS; scores of tile 0
-    issue(kh, 0, kbuf[0]);
-    issue(vh, 0, vbuf[0]);
-    if (nkb > 1) issue(kh, 1, kbuf[1]);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    clear_tail(0, vbuf[0]);
+    // ---- prologue: K_0..K_3 and V_0, V_1 in LDS; scores of tile 0
+    issue(kh, 0, kring[0]);
+    issue(kh, 1, kring[1]);
+    issue(vh, 0, vring[0]);
+    issue(kh, 2, kring[2]);
+    issue(vh, 1, vring[1]);
+    issue(kh, 3, kring[3]);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    if (nkb <= 2) clear_tail(nkb - 1, vring[nkb - 1]);
     __syncthreads();
-    f32x16 s_cur[kBc / 32];
-    scores(kbuf[0], s_cur);
-    __syncthreads();  // kbuf[0] is free for K_2
+    f32x16 sc[kBc / 32];  // scores of the tile whose softmax runs next
+    scores(0, sc);
+    __syncthreads();  // every wave is done with K_0 before K_4 replaces it
 
-    // One key tile: softmax of tile kb (its scores are in s_cur) and, in the
-    // same block so that they overlap, the scores of tile kb+1; then
-    // O^T = alpha * O^T + V^T P^T. MASKED tiles first replace invisible
-    // scores by -inf (a compile-time choice: the interior loop carries no
-    // mask code at all).
-    auto tile = [&](auto masked, int kb) {
-        constexpr bool MASKED = decltype(masked)::value;
-        // In LDS now: K_{kb+1} in kbuf[(kb+1)&1], V_kb in vbuf[kb&1].
-        if (kb + 2 < nkb) issue(kh, kb + 2, kbuf[kb & 1]);
-        if (kb + 1 < nkb) issue(vh, kb + 1, vbuf[(kb + 1) & 1]);
-        const bool has_next = kb + 1 < nkb && active(kb + 1);
-        f32x16 s_next[kBc / 32];
-
-        if (active(kb)) {
-            if constexpr (MASKED) mask(kb, s_cur);
-            bool grow;
-            float alpha;
-            bf16x8 pf[1][kBc / 32][2];
-            auto softmax = [&]() {
-                float mraw = neg_inf();
-#pragma unroll
-                for (int st = 0; st < kBc / 32; ++st)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s_cur[st][r]);
-                mraw = max_with_partner(mraw);
-                // scale >= 0, so the scaled max is scale_log2 * raw max
-                const float mtile = mraw > neg_inf() ? mraw * scale_log2 : neg_inf();
-                grow = mtile > m_run;
-                const float m_new = grow ? mtile : m_run;
-                alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                const float lsum = probs<false, 1>(s_cur, scale_log2, m_run, pf);
-                l_run = l_run * alpha + lsum;
-            };
-            if (has_next) {
-                softmax();
-                scores(kbuf[(kb + 1) & 1], s_next);
-            } else {
-                softmax();
-            }
-
-            // alpha == 1 unless some row's max grew
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-                for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-            }
-            const unsigned char* vt = vbuf[kb & 1];
-#pragma unroll
-            for (int tt = 0; tt < D / 32; ++tt) {
-#pragma unroll
-                for (int st = 0; st < kBc / 32; ++st)
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const unsigned char* base = vt + (st * 32 + h2 * 16) * TL::kRowBytes;
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(base + v_off[tt][0]));
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(base + v_off[tt][1]));
-                        const s16x4 lohi[2] = {lo, hi};
-                        bf16x8 vf;
-                        __builtin_memcpy(&vf, lohi, sizeof(vf));
-                        acc[tt] = mfma(vf, pf[0][st][h2], acc[tt]);
-                    }
-            }
+    // Phases. Global phase s: group 0 runs A(s/2) for even s and B(s/2) for
+    // odd s; group 1 runs one phase later. A(j) is VALU work only (softmax of
+    // tile j, rescale of the output); B(j) is MFMA work only (scores of tile
+    // j+1 from K_{j+1}, then O += P_j V_j), so on every SIMD one wave feeds
+    // the matrix core while the other runs the softmax.
+    // Loads: every phase starts with each wave's share of one tile, V_{s/2+2}
+    // in even phases and K_{(s-1)/2+4} in odd ones, into the ring slot of the
+    // tile four back (its last reader, group 1's B, ended two phases
+    // earlier); every phase ends with vmcnt(4L), so the loads of phase s-4
+    // have landed: K_t is first read in phase 2t-1, V_t in phase 2t+1.
+    auto phase_loads = [&](int s) __attribute__((always_inline)) {
+        if ((s & 1) == 0) {
+            const int t = s / 2 + 2;
+            issue(vh, t, vring[t & 3]);
+        } else {
+            const int t = (s - 1) / 2 + 4;
+            issue(kh, t, kring[t & 3]);
         }
-
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of the next tiles
-        if (kb + 1 < nkb) clear_tail(kb + 1, vbuf[(kb + 1) & 1]);
+    };
+    // The partial last V tile, if any, was issued in phase 2*nkb - 6 (when
+    // nkb > 2) and has landed at the end of phase 2*nkb - 2, one phase before
+    // it is first read; it is cleared there. The scheduling fences keep every
+    // instruction inside its phase: the compiler would otherwise move MFMAs
+    // and VALU work across the barrier and break the pairing of the groups.
+    const int tail_phase = (nkb > 2 && N % kBc != 0 && nkb == nkb_all) ? 2 * nkb - 2 : -1;
+    auto phase_end = [&](int s) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * L));
+        if (s == tail_phase) clear_tail(nkb - 1, vring[(nkb - 1) & 3]);
         __syncthreads();
-#pragma unroll
-        for (int st = 0; st < kBc / 32; ++st) s_cur[st] = s_next[st];
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    int kb = 0;
-    for (; kb < nfull; ++kb) tile(std::false_type{}, kb);
-    for (; kb < nkb; ++kb) tile(std::true_type{}, kb);
+    // Tiles [0, nfull_w) need no mask for this wave: all their keys are < N
+    // and (causal) <= the wave's first query.
+    const int nfull_w = min(CAUSAL ? (qw0 + 1) / kBc : nkb_all, N / kBc);
+    bf16x8 pf[kBc / 32][2];  // P of the current tile, from A(j) to B(j)
+
+    // A(j): VALU only. Softmax of tile j (scores in sc): running max and
+    // sum, bf16 P, and O *= alpha (skipped when no row's max grew: alpha == 1).
+    auto phase_a = [&](int kb) __attribute__((always_inline)) {
+        if (kb > last) return;
+        if (kb >= nfull_w) mask(kb, sc);
+        float mraw = neg_inf();
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, sc[st][r]);
+        mraw = max_with_partner(mraw);
+        // scale >= 0, so the scaled max is scale_log2 * raw max
+        const float mtile = mraw > neg_inf() ? mraw * scale_log2 : neg_inf();
+        const bool grow = mtile > m_run;
+        const float m_new = grow ? mtile : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        bf16x8 p1[1][kBc / 32][2];
+        const float lsum = probs<false, 1>(sc, scale_log2, m_run, p1);
+        l_run = l_run * alpha + lsum;
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) {
+            pf[st][0] = p1[0][st][0];
+            pf[st][1] = p1[0][st][1];
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+        }
+    };
+    constexpr int kPVMfmas = D / 32 * kBc / 16;
+    // B(j): MFMA work only. Scores of tile j+1 from K ring slot kslot, then
+    // O^T += V_j^T P_j^T from V ring slot vslot.
+    auto phase_b = [&](int kb, int kslot, int vslot) __attribute__((always_inline)) {
+        if (kb + 1 <= last) {
+            scores(kslot, sc);
+            // K fragments kReadAhead MFMAs ahead, no further (VGPR budget).
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadAhead, 0);
+#pragma unroll
+            for (int i = 0; i < kKFrags - kReadAhead; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kReadAhead, 0);
+        }
+        if (kb > last) return;
+#pragma unroll
+        for (int tt = 0; tt < D / 32; ++tt) {
+#pragma unroll
+            for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const unsigned off = vslot * TL::kBytes + (st * 32 + h2 * 16) * TL::kRowBytes;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(size_t)(v_off[tt][0] + off));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(size_t)(v_off[tt][1] + off));
+                    const s16x4 lohi[2] = {lo, hi};
+                    bf16x8 vf;
+                    __builtin_memcpy(&vf, lohi, sizeof(vf));
+                    acc[tt] = mfma(vf, pf[st][h2], acc[tt]);
+                }
+        }
+        // V fragments (two transpose reads each) kReadAhead MFMAs ahead.
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kReadAhead, 0);
+#pragma unroll
+        for (int i = 0; i < kPVMfmas - kReadAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kReadAhead, 0);
+    };
+    // Tile j as this wave sees it: A(j) then B(j), each in its global phase
+    // (group 1 one phase later than group 0). R = j mod 4 is a compile-time
+    // constant, so every ring slot is a fixed LDS offset.
+    auto step = [&](auto ring, int kb) __attribute__((always_inline)) {
+        constexpr int R = decltype(ring)::value;
+        const int s = 2 * kb + grp;
+        phase_loads(s);
+        phase_a(kb);
+        phase_end(s);
+        phase_loads(s + 1);
+        phase_b(kb, (R + 1) & 3, R);
+        phase_end(s + 1);
+    };
+
+    if (grp == 1) {  // group 1's idle first phase
+        phase_loads(0);
+        phase_end(0);
+    }
+    // Four tiles per iteration; steps past the last tile (kb >= nkb) only
+    // issue their (empty) loads and meet the barriers.
+    for (int kb = 0; kb < nkb; kb += 4) {
+        step(std::integral_constant<int, 0>{}, kb);
+        step(std::integral_constant<int, 1>{}, kb + 1);
+        step(std::integral_constant<int, 2>{}, kb + 2);
+        step(std::integral_constant<int, 3>{}, kb + 3);
+    }
+    if (grp == 0) {  // group 0's idle last phase
+        const int s_end = 2 * ((nkb + 3) & ~3);
+        phase_loads(s_end);
+        phase_end(s_end);
+    }
+    // No load may still be landing in LDS when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
     // ---- epilogue: O = acc / l, lse = (m2 + log2 l) * ln 2
     const float l_tot = sum_with_partner(l_run);
@@ -338,10 +450,10 @@ template <int D, bool CAUSAL>
 hipError_t launch_one(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
                       int BH, int N, float scale_log2, hipStream_t stream)
 {
-    const int nqb = (N + kBr - 1) / kBr;
+    const int nqb = (N + kBrBf16 - 1) / kBrBf16;
     const dim3 grid((unsigned)((long long)BH * nqb));
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, q, k, v,
-                       o, lse, BH, N, nqb, scale_log2);
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kPPThreads), 0, stream, q, k,
+                       v, o, lse, BH, N, nqb, scale_log2);
     return hipGetLastError();
 }
 

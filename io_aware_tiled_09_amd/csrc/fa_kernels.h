@@ -7,6 +7,7 @@ namespace fa {
 constexpr int kWaves = 4;            // wave64s per workgroup
 constexpr int kBr = kWaves * 32;     // query rows per workgroup (32 per wave)
 constexpr int kBc = 64;              // keys per K/V tile
+constexpr int kBrBf16 = 256;         // query rows per workgroup of the bf16 kernel (8 waves)
 
 // Enqueue one forward pass on `stream`. Shapes are assumed validated:
 // BH = B*H >= 1, N >= 1, d in {64, 128}, BH*ceil(N/kBr) < 2^31.

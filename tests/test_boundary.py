@@ -40,7 +40,7 @@ def test_status_strings():
 
 
 def test_tile_shape():
-    assert fa.fa_tile_rows() == 128 and fa.fa_tile_cols() == 64
+    assert fa.fa_tile_rows() == 256 and fa.fa_tile_cols() == 64
 
 
 def _call(fn=fa.fa_fwd, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
