@@ -1,4 +1,4 @@
-"""Attention-forward oracle (fp64, CPU): TEST INFRASTRUCTURE, not the product.
+"""Attention oracle, forward and backward (fp64, CPU): TEST INFRASTRUCTURE, not the product.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. It loads ``liboracle.so``, built from
@@ -18,6 +18,10 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
   row 0), invariances (key/value permutation, value scaling, per-row score
   shift), rows of P summing to 1, and torch's CPU float64 scaled dot-product
   attention and logsumexp on random inputs.
+* ``attention_bwd``: central finite differences of the forward oracle's loss
+  sum(dO * O) on tiny inputs, torch's CPU float64 autograd of
+  scaled_dot_product_attention, the identities D = rowsum(dO * O) and
+  sum over keys of dK = 0, and the closed forms for N = 1 and scale 0.
 """
 from __future__ import annotations
 
@@ -66,9 +70,12 @@ def _load():
     lib.oracle_attention_rows.argtypes = [_dp, _dp, _dp, ctypes.c_long, ctypes.c_long,
                                           ctypes.c_long, ctypes.c_long, ctypes.c_double,
                                           ctypes.c_int, _lp, ctypes.c_long, _dp, _dp]
+    lib.oracle_attention_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                         ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                         ctypes.c_long, ctypes.c_double, ctypes.c_int]
     for name in ("oracle_softmax_row", "oracle_online_row_two_scale",
                  "oracle_online_row_single_max", "oracle_attention_fwd",
-                 "oracle_attention_rows"):
+                 "oracle_attention_rows", "oracle_attention_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -178,3 +185,22 @@ def attention_rows(q, k, v, scale, causal, rows):
                                          r.ctypes.data_as(_lp), R, _ptr(o), _ptr(lse)),
            "attention_rows")
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, scale, causal, return_delta=False):
+    """Backward pass of standard attention on [B, H, N, d] inputs.
+
+    Returns (dq, dk, dv), each [B, H, N, d], and with return_delta also
+    D [B, H, N] (D_i = sum_j P_ij dP_ij).
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    if not (q.shape == k.shape == v.shape == dout.shape) or q.ndim != 4:
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    delta = np.empty((B, H, N))
+    _check(_load().oracle_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _ptr(delta), B, H, N, d,
+                                        float(scale), int(bool(causal))),
+           "attention_bwd")
+    return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)

@@ -1,5 +1,6 @@
 /*
- * Attention-forward oracle: TEST INFRASTRUCTURE, not part of the product.
+ * Attention oracle (forward and backward): TEST INFRASTRUCTURE, not part of
+ * the product.
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
  * may load this library. It shares no code, header or constant with the HIP
@@ -349,5 +350,111 @@ int oracle_attention_rows(const double *q, const double *k, const double *v,
                           lse_rows + (size_t)bh * R + r);
         }
     free(scratch);
+    return ORACLE_OK;
+}
+
+/*
+ * Backward pass of standard attention for every (b, h), with S, P, dP and
+ * dS materialized for one head at a time.
+ * [P2, "Sizing a tile, and why the backward pass recomputes instead of
+ *  storing": the backward pass needs P again; gradients are the plain
+ *  derivatives of O = softmax(scale * Q K^T + mask) V]
+ *
+ * With L any scalar loss and dO = dL/dO given:
+ *   dV = P^T dO
+ *   dP = dO V^T
+ *   D_i = sum_j P_ij dP_ij            (the softmax Jacobian's row term)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ = scale * dS K,   dK = scale * dS^T Q
+ * Masked entries have P_ij = 0 and so dS_ij = 0.
+ *
+ * q, k, v, dout, dq, dk, dv: [B][H][N][d] fp64; delta (may be NULL):
+ * [B][H][N] fp64, receives D.
+ */
+int oracle_attention_bwd(const double *q, const double *k, const double *v,
+                         const double *dout, double *dq, double *dk,
+                         double *dv, double *delta, long B, long H, long N,
+                         long d, double scale, int causal)
+{
+    if (B < 0 || H < 0 || N < 0 || d < 1)
+        return ORACLE_ERR_ARG;
+    if (B == 0 || H == 0 || N == 0)
+        return ORACLE_OK;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || !isfinite(scale))
+        return ORACLE_ERR_ARG;
+    const size_t nn = (size_t)N * (size_t)N;
+    double *P = (double *)malloc(nn * sizeof(double));
+    double *dS = (double *)malloc(nn * sizeof(double));
+    double *D = (double *)malloc((size_t)N * sizeof(double));
+    if (!P || !dS || !D) {
+        free(P);
+        free(dS);
+        free(D);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (long bh = 0; bh < B * H; ++bh) {
+        const size_t off = (size_t)bh * (size_t)N * (size_t)d;
+        const double *qh = q + off, *kh = k + off, *vh = v + off, *doh = dout + off;
+        double *dqh = dq + off, *dkh = dk + off, *dvh = dv + off;
+        /* P row by row (as in the forward), then dP, D and dS for that row */
+#pragma omp parallel for schedule(dynamic, 4)
+        for (long i = 0; i < N; ++i) {
+            double *Pi = P + (size_t)i * N;
+            double *dSi = dS + (size_t)i * N;
+            double m = -INFINITY;
+            for (long j = 0; j < N; ++j) {
+                double dot = 0.0;
+                for (long t = 0; t < d; ++t)
+                    dot += qh[i * d + t] * kh[j * d + t];
+                Pi[j] = (causal && j > i) ? -INFINITY : scale * dot;
+                if (Pi[j] > m)
+                    m = Pi[j];
+            }
+            double l = 0.0;
+            for (long j = 0; j < N; ++j) {
+                Pi[j] = exp(Pi[j] - m);
+                l += Pi[j];
+            }
+            for (long j = 0; j < N; ++j)
+                Pi[j] /= l;
+            double Di = 0.0;
+            for (long j = 0; j < N; ++j) {
+                double dp = 0.0;
+                for (long t = 0; t < d; ++t)
+                    dp += doh[i * d + t] * vh[j * d + t];
+                dSi[j] = dp; /* dP_ij for now */
+                Di += Pi[j] * dp;
+            }
+            for (long j = 0; j < N; ++j)
+                dSi[j] = Pi[j] * (dSi[j] - Di);
+            D[i] = Di;
+        }
+        /* dQ = scale dS K (rows i) */
+#pragma omp parallel for schedule(static)
+        for (long i = 0; i < N; ++i)
+            for (long t = 0; t < d; ++t) {
+                double acc = 0.0;
+                for (long j = 0; j < N; ++j)
+                    acc += dS[(size_t)i * N + j] * kh[j * d + t];
+                dqh[i * d + t] = scale * acc;
+            }
+        /* dK = scale dS^T Q and dV = P^T dO (rows j) */
+#pragma omp parallel for schedule(static)
+        for (long j = 0; j < N; ++j)
+            for (long t = 0; t < d; ++t) {
+                double ak = 0.0, av = 0.0;
+                for (long i = 0; i < N; ++i) {
+                    ak += dS[(size_t)i * N + j] * qh[i * d + t];
+                    av += P[(size_t)i * N + j] * doh[i * d + t];
+                }
+                dkh[j * d + t] = scale * ak;
+                dvh[j * d + t] = av;
+            }
+        if (delta)
+            memcpy(delta + (size_t)bh * (size_t)N, D, (size_t)N * sizeof(double));
+    }
+    free(P);
+    free(dS);
+    free(D);
     return ORACLE_OK;
 }

@@ -280,3 +280,91 @@ def test_empty_is_a_no_op():
     z = np.zeros((0, 2, 5, 4))
     o, lse = oracle.attention_fwd(z, z, z, 1.0, True)
     assert o.shape == (0, 2, 5, 4) and lse.shape == (0, 2, 5)
+
+
+# ---------------------------------------------------------------- backward pass
+# The backward oracle is pinned to the forward oracle through finite
+# differences (no shared formula), to torch's float64 autograd, and to
+# identities that a dropped term, a wrong sign or a transposed operand breaks.
+
+
+def _bwd_inputs(seed, B=1, H=2, N=6, d=4):
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal((B, H, N, d)) for _ in range(4)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_finite_differences(causal):
+    """dL/dx for L = sum(dO * O) by central differences of the forward oracle."""
+    q, k, v, do = _bwd_inputs(3, B=1, H=1, N=5, d=3)
+    scale = 0.7
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, causal)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention_fwd(q_, k_, v_, scale, causal)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, num, atol=1e-7, rtol=1e-6, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [0.125, 0.5, 2.0])
+def test_bwd_matches_torch_autograd(causal, scale):
+    q, k, v, do = _bwd_inputs(4, B=2, H=2, N=9, d=8)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, causal)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                         scale=scale)
+    o.backward(torch.tensor(do))
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(g, t.grad.numpy(), atol=1e-12, rtol=1e-10)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_delta_is_rowsum_do_o(causal):
+    """D_i = sum_j P_ij dP_ij equals sum_t dO_it O_it (O from the forward)."""
+    q, k, v, do = _bwd_inputs(5, N=11, d=6)
+    _, _, _, delta = oracle.attention_bwd(q, k, v, do, 0.4, causal, return_delta=True)
+    o, _ = oracle.attention_fwd(q, k, v, 0.4, causal)
+    np.testing.assert_allclose(delta, (do * o).sum(-1), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_dk_sums_to_zero_over_keys(causal):
+    """Each row of dS sums to 0 (softmax Jacobian), so sum_j dK_j = 0."""
+    q, k, v, do = _bwd_inputs(6, N=10, d=5)
+    _, dk, dv = oracle.attention_bwd(q, k, v, do, 0.6, causal)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    # and dV collects every row's weight once: sum_j dV_j = sum_i dO_i
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+
+
+def test_bwd_closed_forms():
+    # N = 1: P = 1, so dS = 0 and dV = dO
+    q, k, v, do = _bwd_inputs(7, N=1, d=4)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.5, True)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_allclose(dv, do, atol=0)
+    # scale 0: uniform weights, dQ = dK = 0, dV_j = sum over the rows that see
+    # key j of dO_i / (number of keys row i sees)
+    q, k, v, do = _bwd_inputs(8, N=7, d=3)
+    for causal in (False, True):
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.0, causal)
+        assert np.all(dq == 0) and np.all(dk == 0)
+        N = q.shape[2]
+        expect = np.zeros_like(dv)
+        for i in range(N):
+            n_vis = i + 1 if causal else N
+            for j in range(n_vis):
+                expect[:, :, j] += do[:, :, i] / n_vis
+        np.testing.assert_allclose(dv, expect, atol=1e-14)
