@@ -18,6 +18,9 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
   row 0), invariances (key/value permutation, value scaling, per-row score
   shift), rows of P summing to 1, and torch's CPU float64 scaled dot-product
   attention and logsumexp on random inputs.
+* ``attention_bwd_sampled``: the full ``attention_bwd`` on small inputs and
+  torch's CPU float64 autograd (it evaluates D as dO . O instead of
+  sum_j P_ij dP_ij, and P from lse instead of a stored row).
 * ``attention_bwd``: central finite differences of the forward oracle's loss
   sum(dO * O) on tiny inputs, torch's CPU float64 autograd of
   scaled_dot_product_attention, the identities D = rowsum(dO * O) and
@@ -73,9 +76,14 @@ def _load():
     lib.oracle_attention_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                          ctypes.c_long, ctypes.c_long, ctypes.c_long,
                                          ctypes.c_long, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attention_bwd_sampled.argtypes = [
+        _dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+        ctypes.c_double, ctypes.c_int, _lp, ctypes.c_long, _lp, ctypes.c_long, _lp,
+        ctypes.c_long, _dp, _dp, _dp]
     for name in ("oracle_softmax_row", "oracle_online_row_two_scale",
                  "oracle_online_row_single_max", "oracle_attention_fwd",
-                 "oracle_attention_rows", "oracle_attention_bwd"):
+                 "oracle_attention_rows", "oracle_attention_bwd",
+                 "oracle_attention_bwd_sampled"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -204,3 +212,36 @@ def attention_bwd(q, k, v, dout, scale, causal, return_delta=False):
                                         float(scale), int(bool(causal))),
            "attention_bwd")
     return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)
+
+
+def _idx(a, rows: int, what: str) -> np.ndarray:
+    a = np.asarray(a.numpy() if hasattr(a, "numpy") else a, dtype=np.int64)
+    if a.ndim == 1:
+        a = np.broadcast_to(a, (rows, a.size))
+    if a.ndim != 2 or a.shape[0] != rows:
+        raise ValueError(f"{what} must have one index list per sampled head")
+    return np.ascontiguousarray(a, dtype=np.int64)
+
+
+def attention_bwd_sampled(q, k, v, dout, scale, causal, heads, qrows, krows):
+    """Backward pass on selected heads (flat b*H + h), query rows and key rows.
+
+    heads: [Hs]; qrows: [Hs, R] (or [R]); krows: [Hs, C] (or [C]).
+    Returns (dq_rows [Hs,R,d], dk_rows [Hs,C,d], dv_rows [Hs,C,d]).
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    if not (q.shape == k.shape == v.shape == dout.shape) or q.ndim != 4:
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int64).reshape(-1))
+    qr = _idx(qrows, hs.size, "qrows")
+    kr = _idx(krows, hs.size, "krows")
+    R, C = qr.shape[1], kr.shape[1]
+    dq = np.empty((hs.size, R, d))
+    dk = np.empty((hs.size, C, d))
+    dv = np.empty((hs.size, C, d))
+    _check(_load().oracle_attention_bwd_sampled(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, float(scale), int(bool(causal)),
+        hs.ctypes.data_as(_lp), hs.size, qr.ctypes.data_as(_lp), R, kr.ctypes.data_as(_lp), C,
+        _ptr(dq), _ptr(dk), _ptr(dv)), "attention_bwd_sampled")
+    return dq, dk, dv

@@ -458,3 +458,128 @@ int oracle_attention_bwd(const double *q, const double *k, const double *v,
     free(D);
     return ORACLE_OK;
 }
+
+/*
+ * Backward pass for selected heads, query rows and key rows, for shapes whose
+ * N x N matrices are too large to materialize. The definitions are those of
+ * oracle_attention_bwd; only the order of evaluation differs:
+ *   1. every row i of the head: lse_i and O_i (attention_row), then
+ *      D_i = dO_i . O_i, which equals sum_j P_ij dP_ij because O_i is
+ *      sum_j P_ij V_j;
+ *   2. each sampled query row i: dQ_i = scale * sum_j dS_ij K_j;
+ *   3. each sampled key row j: dV_j = sum_i P_ij dO_i and
+ *      dK_j = scale * sum_i dS_ij Q_i;
+ * with P_ij = exp(scale * Q_i . K_j - lse_i) (0 where masked),
+ * dP_ij = dO_i . V_j and dS_ij = P_ij (dP_ij - D_i).
+ * heads: [Hs] head indices b * H + h; qrows: [Hs][R]; krows: [Hs][C];
+ * dq_rows: [Hs][R][d]; dk_rows, dv_rows: [Hs][C][d].
+ */
+static double dot_d(const double *a, const double *b, long d)
+{
+    double s = 0.0;
+    for (long t = 0; t < d; ++t)
+        s += a[t] * b[t];
+    return s;
+}
+
+int oracle_attention_bwd_sampled(const double *q, const double *k,
+                                 const double *v, const double *dout, long B,
+                                 long H, long N, long d, double scale,
+                                 int causal, const long *heads, long Hs,
+                                 const long *qrows, long R, const long *krows,
+                                 long C, double *dq_rows, double *dk_rows,
+                                 double *dv_rows)
+{
+    if (B < 1 || H < 1 || N < 1 || d < 1 || Hs < 0 || R < 0 || C < 0)
+        return ORACLE_ERR_ARG;
+    if (Hs == 0)
+        return ORACLE_OK;
+    if (!q || !k || !v || !dout || !heads || !isfinite(scale))
+        return ORACLE_ERR_ARG;
+    if ((R > 0 && (!qrows || !dq_rows)) || (C > 0 && (!krows || !dk_rows || !dv_rows)))
+        return ORACLE_ERR_ARG;
+    for (long x = 0; x < Hs; ++x)
+        if (heads[x] < 0 || heads[x] >= B * H)
+            return ORACLE_ERR_ARG;
+    for (long x = 0; x < Hs * R; ++x)
+        if (qrows[x] < 0 || qrows[x] >= N)
+            return ORACLE_ERR_ARG;
+    for (long x = 0; x < Hs * C; ++x)
+        if (krows[x] < 0 || krows[x] >= N)
+            return ORACLE_ERR_ARG;
+    int nt = oracle_num_threads();
+    double *lse = (double *)malloc((size_t)N * sizeof(double));
+    double *D = (double *)malloc((size_t)N * sizeof(double));
+    double *scratch = (double *)malloc((size_t)nt * (2 * (size_t)N + (size_t)d) *
+                                       sizeof(double));
+    if (!lse || !D || !scratch) {
+        free(lse);
+        free(D);
+        free(scratch);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (long x = 0; x < Hs; ++x) {
+        const size_t off = (size_t)heads[x] * (size_t)N * (size_t)d;
+        const double *qh = q + off, *kh = k + off, *vh = v + off, *doh = dout + off;
+        /* step 1: lse_i and D_i for every row */
+#pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i) {
+            int tid = 0;
+#ifdef _OPENMP
+            tid = omp_get_thread_num();
+#endif
+            double *S = scratch + (size_t)tid * (2 * (size_t)N + (size_t)d);
+            double *P = S + N;
+            double *o_row = P + N;
+            attention_row(qh, kh, vh, N, d, scale, causal, i, S, P, o_row, lse + i);
+            D[i] = dot_d(doh + i * d, o_row, d);
+        }
+        /* step 2: sampled rows of dQ */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (long r = 0; r < R; ++r) {
+            const long i = qrows[x * R + r];
+            double *dqi = dq_rows + ((size_t)x * R + r) * (size_t)d;
+            for (long t = 0; t < d; ++t)
+                dqi[t] = 0.0;
+            for (long j = 0; j < N; ++j) {
+                if (causal && j > i)
+                    continue;
+                const double p = exp(scale * dot_d(qh + i * d, kh + j * d, d) - lse[i]);
+                const double dp = dot_d(doh + i * d, vh + j * d, d);
+                const double ds = p * (dp - D[i]);
+                for (long t = 0; t < d; ++t)
+                    dqi[t] += ds * kh[j * d + t];
+            }
+            for (long t = 0; t < d; ++t)
+                dqi[t] *= scale;
+        }
+        /* step 3: sampled rows of dK and dV */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (long c = 0; c < C; ++c) {
+            const long j = krows[x * C + c];
+            double *dkj = dk_rows + ((size_t)x * C + c) * (size_t)d;
+            double *dvj = dv_rows + ((size_t)x * C + c) * (size_t)d;
+            for (long t = 0; t < d; ++t) {
+                dkj[t] = 0.0;
+                dvj[t] = 0.0;
+            }
+            for (long i = 0; i < N; ++i) {
+                if (causal && j > i)
+                    continue;
+                const double p = exp(scale * dot_d(qh + i * d, kh + j * d, d) - lse[i]);
+                const double dp = dot_d(doh + i * d, vh + j * d, d);
+                const double ds = p * (dp - D[i]);
+                for (long t = 0; t < d; ++t) {
+                    dvj[t] += p * doh[i * d + t];
+                    dkj[t] += ds * qh[i * d + t];
+                }
+            }
+            for (long t = 0; t < d; ++t)
+                dkj[t] *= scale;
+        }
+    }
+    free(lse);
+    free(D);
+    free(scratch);
+    return ORACLE_OK;
+}

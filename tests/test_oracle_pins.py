@@ -368,3 +368,31 @@ def test_bwd_closed_forms():
             for j in range(n_vis):
                 expect[:, :, j] += do[:, :, i] / n_vis
         np.testing.assert_allclose(dv, expect, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_sampled_matches_torch_autograd_and_full(causal):
+    """The sampled backward (D from dO . O, P from lse) against torch's float64
+    autograd and the materializing backward, on every head or a subset."""
+    q, k, v, do = _bwd_inputs(9, B=2, H=3, N=37, d=8)
+    scale = 0.35
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                         scale=scale)
+    o.backward(torch.tensor(do))
+    full = oracle.attention_bwd(q, k, v, do, scale, causal)
+    heads = np.array([0, 4, 5])
+    qrows = np.array([[0, 1, 36], [5, 17, 36], [2, 3, 30]])
+    krows = np.array([[0, 20, 36], [0, 1, 2], [36, 35, 9]])
+    dq, dk, dv = oracle.attention_bwd_sampled(q, k, v, do, scale, causal, heads, qrows, krows)
+    tg = [t.grad.numpy().reshape(6, 37, 8) for t in (tq, tk, tv)]
+    fg = [g.reshape(6, 37, 8) for g in full]
+    for x, h in enumerate(heads):
+        for ref in (tg, fg):
+            np.testing.assert_allclose(dq[x], ref[0][h, qrows[x]], atol=1e-12, rtol=1e-10)
+            np.testing.assert_allclose(dk[x], ref[1][h, krows[x]], atol=1e-12, rtol=1e-10)
+            np.testing.assert_allclose(dv[x], ref[2][h, krows[x]], atol=1e-12, rtol=1e-10)
+    with pytest.raises(ValueError):
+        oracle.attention_bwd_sampled(q, k, v, do, scale, causal, [6], [0], [0])
+    with pytest.raises(ValueError):
+        oracle.attention_bwd_sampled(q, k, v, do, scale, causal, [0], [37], [0])
