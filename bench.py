@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the FlashAttention forward pass on one MI355X.
+"""Benchmark of the FlashAttention forward (default) or backward pass on one MI355X.
 
 One step = one forward call (every step of the hot path runs inside the one
 kernel launch) over the long-document causal workload: B=2, H=32, N=8192,
@@ -12,6 +12,11 @@ launched on (torch's current stream, which the binding passes to fa_fwd).
 `value` is useful TFLOP/s over the K calls (4*B*H*N^2*d, halved for causal).
 The CPU baseline times the fp64 oracle on a bounded sample (whole heads of
 the same workload) on this host's cores.
+
+With --pass bwd one step is one backward call (fa_bwd: the D, dK/dV and dQ
+kernels) on the same workload with a seeded N(0,1) dO, O and lse from one
+forward call made before timing; `value` is useful backward TFLOP/s
+(2.5 times the forward's FLOPs: S recomputed, dP, dV, dQ, dK).
 """
 from __future__ import annotations
 
@@ -29,28 +34,36 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k.json")
+TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k.json"),
+                 "bwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_bwd.json")}
+# Sources each pass's kernels are compiled from (the traffic summary is valid
+# only for the exact sources it was taken on).
+PASS_SOURCES = {"fwd": ("fa_common.h", "fa_lds.h", "fa_fwd_bf16.hip"),
+                "bwd": ("fa_common.h", "fa_lds.h", "fa_bwd_bf16.hip")}
+# Kernel names (substrings) rocprofv3 reports for each pass.
+PASS_KERNELS = {"fwd": ("fa_fwd_bf16_kernel",),
+                "bwd": ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel")}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(pass_: str = "fwd") -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_tiled_09_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in PASS_SOURCES[pass_]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(digest: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+def measured_traffic(digest: str, pass_: str = "fwd"):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it
     was taken on this exact kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[pass_]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -69,11 +82,12 @@ def _counter_means(path, counter):
     return {k_: sum(v_) / len(v_) for k_, v_ in by_kernel.items()}
 
 
-def ingest_counters(fetch_csv, write_csv, copy_mib, command):
+def ingest_counters(fetch_csv, write_csv, copy_mib, command, pass_="fwd"):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
-    dispatch) of `command` into HBM bytes per attention launch, each counter
-    scaled by what it reads for the plain device copy of copy_mib MiB that the
-    same command runs (its true traffic is copy_mib MiB read + written)."""
+    dispatch) of `command` into HBM bytes per attention call (the sum over the
+    pass's kernels), each counter scaled by what it reads for the plain device
+    copy of copy_mib MiB that the same command runs (its true traffic is
+    copy_mib MiB read + written)."""
     fetch = _counter_means(fetch_csv, "FETCH_SIZE")
     write = _counter_means(write_csv, "WRITE_SIZE")
 
@@ -83,25 +97,32 @@ def ingest_counters(fetch_csv, write_csv, copy_mib, command):
             raise SystemExit(f"expected one kernel matching {needle!r}, found {len(hits)}")
         return hits[0]
 
-    attn = "fa_fwd_bf16_kernel"
     copy = "copyBuffer"
     true_kib = copy_mib * 1024.0
     f_fetch = true_kib / pick(fetch, copy)
     f_write = true_kib / pick(write, copy)
-    fetch_kib, write_kib = pick(fetch, attn), pick(write, attn)
+    per_kernel = {}
+    for name in PASS_KERNELS[pass_]:
+        fk, wk = pick(fetch, name), pick(write, name)
+        per_kernel[name] = {"fetch_kib_raw": fk, "write_kib_raw": wk,
+                            "hbm_bytes": round((fk * f_fetch + wk * f_write) * 1024.0)}
+    fetch_kib = sum(x["fetch_kib_raw"] for x in per_kernel.values())
+    write_kib = sum(x["write_kib_raw"] for x in per_kernel.values())
     traffic = (fetch_kib * f_fetch + write_kib * f_write) * 1024.0
     out = {
-        "kernel_source_digest": kernel_source_digest(),
+        "kernel_source_digest": kernel_source_digest(pass_),
         "workload": "longdoc8k",
+        "pass": pass_,
         "hbm_bytes_per_launch": round(traffic),
         "fetch_kib_raw": fetch_kib,
         "write_kib_raw": write_kib,
+        "per_kernel": per_kernel,
         "copy_kib_true": true_kib,
         "fetch_scale": f_fetch,
         "write_scale": f_write,
         "command": command,
     }
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(TRAFFIC_FILES[pass_], "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
     return 0
@@ -134,12 +155,41 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     }
 
 
+def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
+    """Time the backward oracle over whole heads of the workload until about budget_s."""
+    import oracle
+    B, H, N, d = q.shape
+    heads, elapsed = 0, 0.0
+    while heads < B * H and elapsed < budget_s:
+        b, h = divmod(heads, H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t0 = time.perf_counter()
+        oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], w.scale, w.causal)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+        log(f"  backward oracle head {heads}: {elapsed:.1f} s")
+    from io_aware_tiled_09_amd.inputs import backward_flops
+    flops = backward_flops(1, heads, N, d, w.causal)
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{heads} of {B * H} heads (all {N} rows each) of {w.name}, fp64 backward "
+                  f"with P and dS materialized; useful backward FLOPs of the sample / "
+                  f"{elapsed:.1f} s wall",
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="longdoc8k")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: one step = one forward call (the default line); bwd: one "
+                         "step = one backward call (fa_bwd) given O and lse")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
@@ -153,7 +203,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.ingest_counters:
         return ingest_counters(*args.ingest_counters, args.copy_kernel_mib or 1024,
-                               args.profile_command)
+                               args.profile_command, args.pass_)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this attention forward has no "
@@ -163,7 +213,8 @@ def main(argv=None):
 
     import torch
     import io_aware_tiled_09_amd as fa
-    from io_aware_tiled_09_amd.inputs import WORKLOADS, make_qkv, useful_flops
+    from io_aware_tiled_09_amd.inputs import (WORKLOADS, backward_flops, make_dout, make_qkv,
+                                              useful_flops)
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -178,11 +229,30 @@ def main(argv=None):
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+    bwd = args.pass_ == "bwd"
+    if bwd and w.dtype != "bf16":
+        print("the backward pass takes bf16 storage only", file=sys.stderr)
+        return 2
 
-    def step():
+    def fwd_step():
         st = fn(dq, dk, dv, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, stream)
         if st != 0:
             raise fa.FAError(st)
+
+    if bwd:
+        do_cpu = make_dout(w)
+        ddo = do_cpu.to(dev)
+        gq, gk, gv = torch.empty_like(dq), torch.empty_like(dq), torch.empty_like(dq)
+        ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        fwd_step()  # O and lse for the backward
+
+        def step():
+            st = fa.fa_bwd(dq, dk, dv, o, lse, ddo, gq, gk, gv, ws, w.B, w.H, w.N, w.d,
+                           w.scale, w.causal, stream)
+            if st != 0:
+                raise fa.FAError(st)
+    else:
+        step = fwd_step
 
     for _ in range(args.warmup):
         step()
@@ -203,7 +273,7 @@ def main(argv=None):
     span_ms = starts[0].elapsed_time(ends[-1])
     avg_launch_ms = sum(per_launch_ms) / K
     med_launch_ms = sorted(per_launch_ms)[K // 2]
-    flops = useful_flops(w.B, w.H, w.N, w.d, w.causal)
+    flops = (backward_flops if bwd else useful_flops)(w.B, w.H, w.N, w.d, w.causal)
     ms_per_step = max(span_ms, 1e-9) / K
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
@@ -219,10 +289,14 @@ def main(argv=None):
         torch.cuda.synchronize()
         log(f"copy kernel: {args.copy_kernel_mib} MiB read + written, 3 times")
 
-    digest = kernel_source_digest()
-    traffic = measured_traffic(digest)
+    digest = kernel_source_digest(args.pass_)
+    traffic = measured_traffic(digest, args.pass_)
+    metric = "attention fwd TFLOP/s (bf16, 1 MI355X) at N=8K d=128 causal; % of MFMA peak"
+    if bwd:
+        metric = ("attention bwd TFLOP/s (bf16, 1 MI355X) at N=8K d=128 causal; % of MFMA peak "
+                  "(useful FLOPs = 2.5x forward)")
     result = {
-        "metric": "attention fwd TFLOP/s (bf16, 1 MI355X) at N=8K d=128 causal; % of MFMA peak",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -236,7 +310,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "seed": w.seed,
-                   "useful_flop_per_call": flops},
+                   "useful_flop_per_call": flops, "pass": args.pass_},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
@@ -246,13 +320,15 @@ def main(argv=None):
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "avg_launch_ms": round(avg_launch_ms, 5),
+            "kernels": list(PASS_KERNELS[args.pass_]),
             "kernel_source_digest": digest,
         },
         "cpu_baseline": None,
     }
     if args.cpu_budget > 0:
         log("timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        result["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do_cpu, args.cpu_budget) if bwd
+                                  else cpu_baseline(w, q, k, v, args.cpu_budget))
     print(json.dumps(result), flush=True)
     return 0
 

@@ -46,7 +46,7 @@ typedef enum fa_status {
     FA_ERR_UNSUPPORTED_HEAD_DIM = 3,/* d is not 64 or 128                          */
     FA_ERR_BAD_SCALE = 4,           /* scale negative, NaN or infinite             */
     FA_ERR_MISALIGNED = 5,          /* q/k/v/o not 16-byte aligned, lse not 4-byte */
-    FA_ERR_ALIASING = 6,            /* o or lse overlaps q, k, v or each other     */
+    FA_ERR_ALIASING = 6,            /* an output overlaps an input or an output    */
     FA_ERR_LAUNCH = 7,              /* the HIP runtime rejected the launch         */
     FA_ERR_TOO_LARGE = 8            /* B*H*ceil(N/128) workgroups exceed 2^31 - 1  */
 } fa_status;
@@ -75,6 +75,30 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
                float *lse, int B, int H, int N, int d, float scale, int causal,
                void *stream);
+
+/*
+ * bf16 attention backward pass: dq, dk, dv from dout for the forward pass
+ * fa_fwd computed with the same q, k, v, scale and causal flag.
+ * [Flash Attention Optimization (aicomputerinstitute.com), "Sizing a tile,
+ *  and why the backward pass recomputes instead of storing": P is
+ *  recomputed block by block from q, k and the forward's per-row lse]
+ *
+ * With S = scale * q k^T (+ mask) and P = softmax(S) row-wise:
+ *     dv = P^T dout,  dS = P * (dout v^T - D),  D_i = sum_t dout_it o_it,
+ *     dq = scale * dS k,  dk = scale * dS^T q.
+ * q, k, v, o, dout: const bf16 [B][H][N][d] (o = fa_fwd's output);
+ * lse: const fp32 [B][H][N] (fa_fwd's lse, natural log);
+ * dq, dk, dv: bf16 [B][H][N][d] outputs (round-to-nearest-even);
+ * ws: fp32 workspace of B*H*N elements, overwritten (holds D);
+ * every other argument as in fa_fwd. All pointers are DEVICE pointers; the
+ * outputs and ws must not overlap any input or each other
+ * (FA_ERR_ALIASING). Products take bf16 operands (P and dS rounded to bf16)
+ * and accumulate in fp32. Launches three kernels on `stream` and returns.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const float *lse, const void *dout, void *dq, void *dk, void *dv,
+           float *ws, int B, int H, int N, int d, float scale, int causal,
+           void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -1,13 +1,15 @@
-"""FlashAttention forward for MI355X (gfx950).
+"""FlashAttention forward (and backward) for MI355X (gfx950).
 
 The hot path is the HIP library ``libfa.so`` (C ABI in ``include/fa.h``);
 this package only marshals arguments to it (``fa_fwd``, ``fa_fwd_f32``,
-``fa_status_string``) and offers ``attention()``, which allocates the outputs
-with torch and calls ``fa_fwd``. Seeded synthetic inputs live in
-``io_aware_tiled_09_amd.inputs``.
+``fa_bwd``, ``fa_status_string``) and offers ``attention()`` and
+``attention_backward()``, which allocate the outputs with torch and call the
+library. Seeded synthetic inputs live in ``io_aware_tiled_09_amd.inputs``.
 """
-from ._binding import (EXPORTS, FA_OK, FAError, LIB_PATH, attention, fa_fwd, fa_fwd_f32,
-                       fa_status_string, fa_tile_cols, fa_tile_rows, load)
+from ._binding import (EXPORTS, FA_OK, FAError, LIB_PATH, attention, attention_backward,
+                       fa_bwd, fa_fwd, fa_fwd_f32, fa_status_string, fa_tile_cols, fa_tile_rows,
+                       load)
 
-__all__ = ["attention", "fa_fwd", "fa_fwd_f32", "fa_status_string", "fa_tile_rows",
-           "fa_tile_cols", "FAError", "FA_OK", "EXPORTS", "LIB_PATH", "load"]
+__all__ = ["attention", "attention_backward", "fa_fwd", "fa_fwd_f32", "fa_bwd",
+           "fa_status_string", "fa_tile_rows", "fa_tile_cols", "FAError", "FA_OK", "EXPORTS",
+           "LIB_PATH", "load"]

@@ -21,7 +21,8 @@ STATUS_NAMES = {
     4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_MISALIGNED", 6: "FA_ERR_ALIASING", 7: "FA_ERR_LAUNCH",
     8: "FA_ERR_TOO_LARGE",
 }
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_status_string", "fa_tile_rows", "fa_tile_cols")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string", "fa_tile_rows",
+           "fa_tile_cols")
 
 
 class FAError(RuntimeError):
@@ -44,6 +45,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         fn.restype = i
+    lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_tile_rows.restype = i
@@ -87,6 +90,15 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
                                  _stream(stream, (q, k, v, o, lse))))
 
 
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, d, scale, causal, stream=None) -> int:
+    """C fa_bwd: bf16 q, k, v, o, dout, dq, dk, dv [B,H,N,d], fp32 lse and workspace
+    ws [B,H,N] device tensors (or raw device addresses). Returns the fa_status code."""
+    return int(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), int(B), int(H), int(N),
+                             int(d), float(scale), int(bool(causal)),
+                             _stream(stream, (q, k, v, o, lse, dout))))
+
+
 def fa_status_string(status: int) -> str:
     return load().fa_status_string(int(status)).decode()
 
@@ -126,3 +138,27 @@ def attention(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None
     if st != FA_OK:
         raise FAError(st)
     return out, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
+    """Allocate dq, dk, dv and the workspace with torch and run the backward pass.
+
+    q, k, v, o, dout: contiguous bf16 [B, H, N, d] CUDA tensors (o and lse from
+    the forward pass with the same q, k, v, causal and scale). Returns
+    (dq, dk, dv); raises FAError on a status.
+    """
+    import torch
+    ts = (q, k, v, o, dout)
+    if any(t.shape != q.shape for t in ts) or q.dim() != 4:
+        raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape")
+    if any(t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() for t in ts):
+        raise ValueError("q, k, v, o, dout must be contiguous bf16 GPU tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, d, scale, causal, stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return dq, dk, dv

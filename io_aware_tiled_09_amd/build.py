@@ -9,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = [os.path.join(PKG, "csrc", "fa_fwd_bf16.hip"),
+           os.path.join(PKG, "csrc", "fa_bwd_bf16.hip"),
            os.path.join(PKG, "csrc", "fa_fwd_f32.hip"),
            os.path.join(PKG, "csrc", "fa_api.cpp")]
 ARCH = "gfx950"

@@ -95,6 +95,49 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N, int d,
+           float scale, int causal, void* stream)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return FA_ERR_BAD_SHAPE;
+    if (B == 0 || H == 0 || N == 0)
+        return FA_OK;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws)
+        return FA_ERR_NULL_PTR;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!isfinite(scale) || scale < 0.0f)
+        return FA_ERR_BAD_SCALE;
+    const long long nqb = ((long long)N + fa::kBr - 1) / fa::kBr;
+    if ((long long)B * H * nqb > 0x7fffffffLL)
+        return FA_ERR_TOO_LARGE;
+    auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
+    if ((addr(q) | addr(k) | addr(v) | addr(o) | addr(dout) | addr(dq) | addr(dk) | addr(dv)) & 15u)
+        return FA_ERR_MISALIGNED;
+    if ((addr(lse) | addr(ws)) & 3u)
+        return FA_ERR_MISALIGNED;
+    const uintptr_t tb = (uintptr_t)B * (uintptr_t)H * (uintptr_t)N * (uintptr_t)d * 2;
+    const uintptr_t rb = (uintptr_t)B * (uintptr_t)H * (uintptr_t)N * sizeof(float);
+    const Range in[6] = {{addr(q), addr(q) + tb},     {addr(k), addr(k) + tb},
+                         {addr(v), addr(v) + tb},     {addr(o), addr(o) + tb},
+                         {addr(lse), addr(lse) + rb}, {addr(dout), addr(dout) + tb}};
+    const Range out[4] = {{addr(dq), addr(dq) + tb}, {addr(dk), addr(dk) + tb},
+                          {addr(dv), addr(dv) + tb}, {addr(ws), addr(ws) + rb}};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(out[a], in[b]))
+                return FA_ERR_ALIASING;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(out[a], out[b]))
+                return FA_ERR_ALIASING;
+    }
+    const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, ws, B * H, N, d,
+                                             kernel_scale(scale), scale, causal != 0,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_status_string(int status)
 {
     switch (status) {
@@ -104,7 +147,7 @@ const char* fa_status_string(int status)
     case FA_ERR_UNSUPPORTED_HEAD_DIM: return "head dimension d must be 64 or 128";
     case FA_ERR_BAD_SCALE: return "scale must be finite and >= 0";
     case FA_ERR_MISALIGNED: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_ALIASING: return "o or lse overlaps an input or each other";
+    case FA_ERR_ALIASING: return "an output overlaps an input or another output";
     case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case FA_ERR_TOO_LARGE: return "too many workgroups (B*H*ceil(N/128) >= 2^31)";
     default: return "unknown status";

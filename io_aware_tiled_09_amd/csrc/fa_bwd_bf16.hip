@@ -1,0 +1,470 @@
+// Attention backward pass for bf16 storage on CDNA4 (gfx950, MI355X).
+//
+// Method: [Flash Attention Optimization (aicomputerinstitute.com), "Sizing a
+// tile, and why the backward pass recomputes instead of storing"]: the
+// forward pass keeps only per-row statistics (here the log-sum-exp), and the
+// backward pass recomputes each block of P from Q, K and that statistic
+// instead of reading a stored N x N matrix. The gradients are the plain
+// derivatives of O = softmax(scale * Q K^T + mask) V:
+//     dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij = sum_t dO_it O_it,
+//     dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// gfx950 mapping (this file's own design): three kernels, no atomics.
+//  * delta: D_i = sum_t dO_it O_it per row into a workspace (HBM-bound).
+//  * dkdv: one workgroup per 128 keys of a head (4 waves x 32 keys); the
+//    wave keeps its K and V rows as MFMA B operands in VGPRs and streams
+//    64-query tiles of Q and dO through LDS. S = Q K^T and dP = dO V^T come
+//    out of v_mfma_f32_32x32x16_bf16 with one key per lane column, so P and
+//    dS (bf16) are directly the B operands of dV^T += dO^T P and
+//    dK^T += Q^T dS, whose A operands are transpose reads of the Q and dO
+//    tiles (ds_read_b64_tr_b16) -- the forward kernel's layout with the
+//    roles of queries and keys exchanged.
+//  * dq: one workgroup per 128 queries (4 waves x 32 rows), streaming K and
+//    V tiles like the forward kernel: S^T = K Q^T and dP^T = V dO^T, then
+//    dQ^T += K^T dS^T with K^T from transpose reads of the K tile.
+//  * P is recomputed as exp2(s * scale*log2(e) - lse*log2(e)); masked and
+//    out-of-range entries are 0. dS is formed in fp32 and rounded to bf16 for
+//    its products; all products accumulate in fp32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_common.h"
+#include "fa_lds.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = kBwdWaves * 64;
+constexpr int kBwdRows = kBwdWaves * 32;     // queries (dq) or keys (dkdv) per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- delta
+// D_i = sum_t dO_it O_it: 16 lanes per row, D/16 elements per lane.
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const __bf16* __restrict__ o,
+                                                           const __bf16* __restrict__ dout,
+                                                           float* __restrict__ delta,
+                                                           long long rows)
+{
+    constexpr int kPer = D / 16;
+    const long long row = (long long)blockIdx.x * 16 + threadIdx.x / 16;
+    const int j = threadIdx.x % 16;
+    float s = 0.f;
+    if (row < rows) {
+        const __bf16* orow = o + row * D + j * kPer;
+        const __bf16* drow = dout + row * D + j * kPer;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) s += (float)orow[t] * (float)drow[t];
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+    if (row < rows && j == 0) delta[row] = s;
+}
+
+// Store 32 columns x 4 of a 32x32 accumulator tile for this lane's row:
+// acc[t][g*4+i] is column t*32 + g*8 + lh*4 + i.
+template <int D>
+__device__ inline void store_row(__bf16* row, const f32x16 (&acc)[D / 32], float mul, int lh)
+{
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            store4(row + t * 32 + g * 8 + lh * 4, acc[t][g * 4 + 0] * mul, acc[t][g * 4 + 1] * mul,
+                   acc[t][g * 4 + 2] * mul, acc[t][g * 4 + 3] * mul);
+}
+
+// Direct loads of one 64-row tile of `src` (rows >= N read as 0 / are not
+// written) into LDS, this wave's share.
+template <typename TL>
+__device__ inline void issue_tile(const __bf16* src, int t, int N, unsigned char* dst,
+                                  const int* ld_off, int wave)
+{
+    constexpr int D = TL::kRowBytes / 2;
+    const int j0 = t * kBc;
+    const unsigned bytes = (unsigned)min(kBc, N - j0) * TL::kRowBytes;
+    const i32x4 rs = buffer_rsrc(src + (size_t)j0 * D, bytes);
+#pragma unroll
+    for (int it = 0; it < TL::kLoadsPerWave; ++it)
+        lds_dma16(rs, ld_off[it], lds_addr(dst + (wave * TL::kLoadsPerWave + it) * 1024));
+}
+
+// Rows of a partial last tile past the sequence end are cleared once the
+// tile has landed: their weights are 0, and 0 * NaN would leak.
+template <typename TL>
+__device__ inline void clear_tile_tail(int t, int N, unsigned char* dst, int tid)
+{
+    const int rows = N - t * kBc;
+    if (rows >= kBc) return;
+    for (int x = tid; x < (kBc - rows) * TL::kChunks; x += kBwdThreads) {
+        const int row = rows + x / TL::kChunks;
+        *reinterpret_cast<bf16x8*>(dst + row * TL::kRowBytes + (x % TL::kChunks) * 16) = bf16x8{};
+    }
+}
+
+// ---------------------------------------------------------------- dk, dv
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                        const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                        const float* __restrict__ lse, const float* __restrict__ delta,
+                        __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH, int N,
+                        int nkblk, float scale_log2, float scale)
+{
+    using TL = Tile<D, kBwdWaves>;
+    constexpr int L = TL::kLoadsPerWave;
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf[2][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char dobuf[2][TL::kBytes];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][kBc];  // lse * log2(e) per query
+    __shared__ __attribute__((aligned(16))) float dl_s[2][kBc];   // D per query
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int li = lane & 31;
+    const int lh = lane >> 5;
+
+    // Key blocks in ascending order: for causal attention the first key
+    // blocks see the most queries, so the heaviest work starts first.
+    int kblk, bh;
+    block_coords<false>(blockIdx.x, BH, nkblk, kblk, bh);
+    const size_t head_off = (size_t)bh * (size_t)N * D;
+    const __bf16* qh = q + head_off;
+    const __bf16* doh = dout + head_off;
+    const float* lseh = lse + (size_t)bh * N;
+    const float* dlh = delta + (size_t)bh * N;
+
+    const int k0 = kblk * kBwdRows;
+    const int kw0 = k0 + wave * 32;   // first key of this wave
+    const int kj = kw0 + li;          // this lane's key
+
+    // K and V rows of this lane's key as B operands (8 d values per lane).
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const __bf16* krow = k + head_off + (size_t)kj * D;
+        const __bf16* vrow = v + head_off + (size_t)kj * D;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            kf[c] = kj < N ? *reinterpret_cast<const bf16x8*>(krow + c * 16 + lh * 8) : bf16x8{};
+            vf[c] = kj < N ? *reinterpret_cast<const bf16x8*>(vrow + c * 16 + lh * 8) : bf16x8{};
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+
+    int ld_off[L];
+#pragma unroll
+    for (int it = 0; it < L; ++it) ld_off[it] = TL::load_offset(wave, it, lane);
+    int f_off[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) f_off[c] = TL::frag_offset(li, 2 * c + lh);
+    int t_off[D / 32][2];
+#pragma unroll
+    for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) t_off[tt][s] = TL::tr_offset(tt, s, lane);
+
+    const int nqt = (N + kBc - 1) / kBc;
+    // Causal: query tiles before the block's first key see none of its keys.
+    const int t0 = CAUSAL ? k0 / kBc : 0;
+
+    // Per-query statistics of tile t: threads 0..63 fetch lse, 64..127 D.
+    auto fetch_stats = [&](int t) __attribute__((always_inline)) {
+        const int qq = t * kBc + (tid & 63);
+        float x = 0.f;
+        if (tid < 2 * kBc && qq < N) x = tid < kBc ? lseh[qq] * kLog2e : dlh[qq];
+        return x;
+    };
+    auto put_stats = [&](int t, float x) __attribute__((always_inline)) {
+        if (tid < kBc) lse_s[t & 1][tid] = x;
+        else if (tid < 2 * kBc) dl_s[t & 1][tid - kBc] = x;
+    };
+
+    f32x16 acc_k[D / 32], acc_v[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+        acc_k[t] = f32x16{};
+        acc_v[t] = f32x16{};
+    }
+
+    if (t0 < nqt) {
+        issue_tile<TL>(qh, t0, N, qbuf[t0 & 1], ld_off, wave);
+        issue_tile<TL>(doh, t0, N, dobuf[t0 & 1], ld_off, wave);
+        put_stats(t0, fetch_stats(t0));
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+        clear_tile_tail<TL>(t0, N, qbuf[t0 & 1], tid);
+        clear_tile_tail<TL>(t0, N, dobuf[t0 & 1], tid);
+        __syncthreads();
+    }
+
+    for (int t = t0; t < nqt; ++t) {
+        const int b = t & 1;
+        float next_stats = 0.f;
+        if (t + 1 < nqt) {
+            issue_tile<TL>(qh, t + 1, N, qbuf[b ^ 1], ld_off, wave);
+            issue_tile<TL>(doh, t + 1, N, dobuf[b ^ 1], ld_off, wave);
+            next_stats = fetch_stats(t + 1);
+        }
+        // Causal: a wave whose keys all follow every query of the tile skips it.
+        const bool active = !CAUSAL || t * kBc + kBc - 1 >= kw0;
+        if (active) {
+            const unsigned char* qt = qbuf[b];
+            const unsigned char* dt = dobuf[b];
+            // S = Q K^T and dP = dO V^T for the tile's 64 queries: lane = key,
+            // 16 queries per 32-query sub-tile.
+            f32x16 s[kBc / 32], dp[kBc / 32];
+#pragma unroll
+            for (int st = 0; st < kBc / 32; ++st) {
+                s[st] = f32x16{};
+                dp[st] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    const int off = st * 32 * TL::kRowBytes + f_off[c];
+                    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + off);
+                    const bf16x8 da = *reinterpret_cast<const bf16x8*>(dt + off);
+                    s[st] = mfma(qa, kf[c], s[st]);
+                    dp[st] = mfma(da, vf[c], dp[st]);
+                }
+            }
+            // P = exp2(s c - lse2_q) (0 where masked), dS = P (dP - D_q).
+            const bool need_mask = (CAUSAL && t * kBc < kw0 + 31) || t * kBc + kBc > N;
+            bf16x8 pf[kBc / 32][2], dsf[kBc / 32][2];
+#pragma unroll
+            for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int qloc = st * 32 + g * 8 + lh * 4;  // queries qloc .. qloc+3
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][qloc]);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_s[b][qloc]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = g * 4 + i;
+                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], scale_log2, -l4[i]));
+                        if (need_mask) {
+                            const int qq = t * kBc + qloc + i;
+                            const bool ok = qq < N && (!CAUSAL || qq >= kj);
+                            p = ok ? p : 0.f;
+                        }
+                        const float ds = p * (dp[st][r] - d4[i]);
+                        pf[st][r >> 3][r & 7] = (__bf16)p;
+                        dsf[st][r >> 3][r & 7] = (__bf16)ds;
+                    }
+                }
+            // dV^T += dO^T P and dK^T += Q^T dS, A operands by transpose reads.
+#pragma unroll
+            for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+                for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int base = (st * 32 + h2 * 16) * TL::kRowBytes;
+                        const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(dt + base + t_off[tt][0]));
+                        const s16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(dt + base + t_off[tt][1]));
+                        const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(qt + base + t_off[tt][0]));
+                        const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(qt + base + t_off[tt][1]));
+                        const s16x4 dpair[2] = {dlo, dhi}, qpair[2] = {qlo, qhi};
+                        bf16x8 da, qa;
+                        __builtin_memcpy(&da, dpair, sizeof(da));
+                        __builtin_memcpy(&qa, qpair, sizeof(qa));
+                        acc_v[tt] = mfma(da, pf[st][h2], acc_v[tt]);
+                        acc_k[tt] = mfma(qa, dsf[st][h2], acc_k[tt]);
+                    }
+        }
+        if (t + 1 < nqt) {
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // this wave's loads of tile t+1
+            clear_tile_tail<TL>(t + 1, N, qbuf[b ^ 1], tid);
+            clear_tile_tail<TL>(t + 1, N, dobuf[b ^ 1], tid);
+            put_stats(t + 1, next_stats);
+        }
+        __syncthreads();
+    }
+
+    if (kj < N) {
+        store_row<D>(dk + head_off + (size_t)kj * D, acc_k, scale, lh);
+        store_row<D>(dv + head_off + (size_t)kj * D, acc_v, 1.0f, lh);
+    }
+}
+
+// ---------------------------------------------------------------- dq
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                      const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                      const float* __restrict__ lse, const float* __restrict__ delta,
+                      __bf16* __restrict__ dq, int BH, int N, int nqb, float scale_log2,
+                      float scale)
+{
+    using TL = Tile<D, kBwdWaves>;
+    constexpr int L = TL::kLoadsPerWave;
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TL::kBytes];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int li = lane & 31;
+    const int lh = lane >> 5;
+
+    int qb, bh;
+    block_coords<CAUSAL>(blockIdx.x, BH, nqb, qb, bh);
+    const size_t head_off = (size_t)bh * (size_t)N * D;
+    const __bf16* kh = k + head_off;
+    const __bf16* vh = v + head_off;
+
+    const int q0 = qb * kBwdRows;
+    const int qw0 = q0 + wave * 32;
+    const int qi = qw0 + li;
+
+    // Q and dO rows of this lane's query as B operands.
+    bf16x8 qf[D / 16], df[D / 16];
+    {
+        const __bf16* qrow = q + head_off + (size_t)qi * D;
+        const __bf16* drow = dout + head_off + (size_t)qi * D;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            qf[c] = qi < N ? *reinterpret_cast<const bf16x8*>(qrow + c * 16 + lh * 8) : bf16x8{};
+            df[c] = qi < N ? *reinterpret_cast<const bf16x8*>(drow + c * 16 + lh * 8) : bf16x8{};
+        }
+    }
+    const float lse2 = qi < N ? lse[(size_t)bh * N + qi] * kLog2e : 0.f;
+    const float dlt = qi < N ? delta[(size_t)bh * N + qi] : 0.f;
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+
+    int ld_off[L];
+#pragma unroll
+    for (int it = 0; it < L; ++it) ld_off[it] = TL::load_offset(wave, it, lane);
+    int f_off[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) f_off[c] = TL::frag_offset(li, 2 * c + lh);
+    int t_off[D / 32][2];
+#pragma unroll
+    for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) t_off[tt][s] = TL::tr_offset(tt, s, lane);
+
+    const int nkb_all = (N + kBc - 1) / kBc;
+    const int nkb = CAUSAL ? min(nkb_all, (q0 + kBwdRows - 1) / kBc + 1) : nkb_all;
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+
+    issue_tile<TL>(kh, 0, N, kbuf[0], ld_off, wave);
+    issue_tile<TL>(vh, 0, N, vbuf[0], ld_off, wave);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    clear_tile_tail<TL>(0, N, kbuf[0], tid);
+    clear_tile_tail<TL>(0, N, vbuf[0], tid);
+    __syncthreads();
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int b = kb & 1;
+        if (kb + 1 < nkb) {
+            issue_tile<TL>(kh, kb + 1, N, kbuf[b ^ 1], ld_off, wave);
+            issue_tile<TL>(vh, kb + 1, N, vbuf[b ^ 1], ld_off, wave);
+        }
+        const bool active = !CAUSAL || kb * kBc <= qw0 + 31;
+        if (active) {
+            const unsigned char* kt = kbuf[b];
+            const unsigned char* vt = vbuf[b];
+            // S^T = K Q^T and dP^T = V dO^T: lane = query, 16 keys per sub-tile.
+            f32x16 s[kBc / 32], dp[kBc / 32];
+#pragma unroll
+            for (int st = 0; st < kBc / 32; ++st) {
+                s[st] = f32x16{};
+                dp[st] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    const int off = st * 32 * TL::kRowBytes + f_off[c];
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
+                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + off);
+                    s[st] = mfma(ka, qf[c], s[st]);
+                    dp[st] = mfma(va, df[c], dp[st]);
+                }
+            }
+            const bool need_mask = (CAUSAL && kb * kBc + kBc - 1 > qw0) || kb * kBc + kBc > N;
+            bf16x8 dsf[kBc / 32][2];
+#pragma unroll
+            for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], scale_log2, -lse2));
+                    if (need_mask) {
+                        const int j = kb * kBc + score_key(st, r, lh);
+                        const bool ok = j < N && (!CAUSAL || j <= qi);
+                        p = ok ? p : 0.f;
+                    }
+                    dsf[st][r >> 3][r & 7] = (__bf16)(p * (dp[st][r] - dlt));
+                }
+            // dQ^T += K^T dS^T, K^T by transpose reads of the K tile.
+#pragma unroll
+            for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+                for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int base = (st * 32 + h2 * 16) * TL::kRowBytes;
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(kt + base + t_off[tt][0]));
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(kt + base + t_off[tt][1]));
+                        const s16x4 pair[2] = {lo, hi};
+                        bf16x8 ka;
+                        __builtin_memcpy(&ka, pair, sizeof(ka));
+                        acc[tt] = mfma(ka, dsf[st][h2], acc[tt]);
+                    }
+        }
+        if (kb + 1 < nkb) {
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            clear_tile_tail<TL>(kb + 1, N, kbuf[b ^ 1], tid);
+            clear_tile_tail<TL>(kb + 1, N, vbuf[b ^ 1], tid);
+        }
+        __syncthreads();
+    }
+
+    if (qi < N) store_row<D>(dq + head_off + (size_t)qi * D, acc, scale, lh);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_one(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
+                          const float* lse, const __bf16* dout, __bf16* dq, __bf16* dk,
+                          __bf16* dv, float* delta, int BH, int N, float scale_log2, float scale,
+                          hipStream_t stream)
+{
+    const long long rows = (long long)BH * N;
+    hipLaunchKernelGGL((fa_bwd_delta_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                       stream, o, dout, delta, rows);
+    const int nblk = (N + kBwdRows - 1) / kBwdRows;
+    const dim3 grid((unsigned)((long long)BH * nblk));
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, q, k,
+                       v, dout, lse, delta, dk, dv, BH, N, nblk, scale_log2, scale);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, q, k, v,
+                       dout, lse, delta, dq, BH, N, nblk, scale_log2, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* delta, int BH, int N, int d, float scale_log2, float scale,
+                           bool causal, hipStream_t stream)
+{
+    auto c = [](const void* p) { return static_cast<const __bf16*>(p); };
+    auto m = [](void* p) { return static_cast<__bf16*>(p); };
+    if (d == 64)
+        return causal ? launch_bwd_one<64, true>(c(q), c(k), c(v), c(o), lse, c(dout), m(dq), m(dk),
+                                                 m(dv), delta, BH, N, scale_log2, scale, stream)
+                      : launch_bwd_one<64, false>(c(q), c(k), c(v), c(o), lse, c(dout), m(dq),
+                                                  m(dk), m(dv), delta, BH, N, scale_log2, scale,
+                                                  stream);
+    return causal ? launch_bwd_one<128, true>(c(q), c(k), c(v), c(o), lse, c(dout), m(dq), m(dk),
+                                              m(dv), delta, BH, N, scale_log2, scale, stream)
+                  : launch_bwd_one<128, false>(c(q), c(k), c(v), c(o), lse, c(dout), m(dq), m(dk),
+                                               m(dv), delta, BH, N, scale_log2, scale, stream);
+}
+
+}  // namespace fa

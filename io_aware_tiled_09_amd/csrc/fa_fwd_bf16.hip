@@ -57,6 +57,7 @@
 #include <type_traits>
 
 #include "fa_common.h"
+#include "fa_lds.h"
 
 namespace fa {
 namespace {
@@ -72,63 +73,13 @@ constexpr int kSchedDsRead = 0x100;
 constexpr int kReadAhead = 6;
 static_assert(kBrBf16 == kPPWaves * 32, "32 query rows per wave");
 
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-template <int D>
-struct Tile {
-    static constexpr int kRowBytes = D * 2;                 // one key row, bf16
-    static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
-    static constexpr int kBytes = kBc * kRowBytes;          // one K or V tile
-    static constexpr int kRowsPerLoad = 1024 / kRowBytes;   // rows per wave-wide load
-    static constexpr int kLoadsPerWave = kBytes / 1024 / kPPWaves;
-    static_assert(kLoadsPerWave * 1024 * kPPWaves == kBytes, "tile must split over waves");
-
-    // Physical 16-byte chunk slot of logical chunk c in tile row r is c ^ swz(r).
-    // D = 128 (16 chunks/row, rows 256 B apart): a bijection of r mod 16 whose
-    //   value over 4 consecutive rows differs in bits 2-3.
-    // D = 64 (8 chunks/row, rows 128 B apart, so row parity picks the bank
-    //   half): a bijection of (r >> 1) mod 8 whose value over rows r, r+2
-    //   differs in bit 2.
-    __device__ static int swz(int r) {
-        if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-        else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-    }
-};
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// s_waitcnt immediate (gfx9 encoding) with only vmcnt constrained (n < 16):
-// expcnt and lgkmcnt keep their maximum values.
-constexpr int wait_vmcnt(int n) { return 0x0F70 | n; }
-
-// Raw buffer resource over [base, base + bytes): offsets past `bytes` read 0.
-__device__ inline i32x4 buffer_rsrc(const void* base, unsigned bytes) {
-    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-    return i32x4{(int)(unsigned)a, (int)(unsigned)(a >> 32), (int)bytes, 0x00020000};
-}
-
-__device__ inline unsigned lds_addr(const void* p) {
-    return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// One wave-wide load straight into LDS: lane i's 16 bytes at byte offset
-// `voff` of the buffer land at LDS address base + 16*i. Issued as inline asm
-// so that the compiler's wait-count pass does not treat later LDS reads of
-// other ring slots as dependent on it; the kernel waits for these loads
-// explicitly (vmcnt) before the barrier that publishes a tile. M0 carries
-// the LDS base; the kernel uses M0 for nothing else.
-__device__ inline void lds_dma16(i32x4 rsrc, unsigned voff, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(lds_base), "s"(rsrc) : "memory");
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                         const __bf16* __restrict__ v, __bf16* __restrict__ o,
                         float* __restrict__ lse, int BH, int N, int nqb, float scale_log2)
 {
-    using TL = Tile<D>;
+    using TL = Tile<D, kPPWaves>;
     constexpr int L = TL::kLoadsPerWave;
     // Tile t of K lives in kring[t % 4], tile t of V in vring[t % 4]; rows
     // are swizzled (Tile::swz).
@@ -178,12 +129,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // i % kChunks, which holds logical chunk (i % kChunks) ^ swz(row).
     int ld_off[L];
 #pragma unroll
-    for (int it = 0; it < L; ++it) {
-        const int n = wave * L + it;
-        const int row = n * TL::kRowsPerLoad + lane / TL::kChunks;
-        const int lchunk = (lane % TL::kChunks) ^ TL::swz(row);
-        ld_off[it] = row * TL::kRowBytes + lchunk * 16;
-    }
+    for (int it = 0; it < L; ++it) ld_off[it] = TL::load_offset(wave, it, lane);
     // This wave's share of tile t of `src` into `dst`. A tile past the last
     // one is still issued, with an empty buffer range (nothing is read), so
     // that every wave issues exactly L loads per phase and the vmcnt
@@ -220,8 +166,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // K fragment (A operand of S^T): key row st*32 + li, logical chunk 2c + lh.
     unsigned k_off[D / 16];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-        k_off[c] = kbase + li * TL::kRowBytes + (((2 * c + lh) ^ TL::swz(li)) * 16);
+    for (int c = 0; c < D / 16; ++c) k_off[c] = kbase + TL::frag_offset(li, 2 * c + lh);
 
     // V^T fragment (A operand of O^T += V^T P^T) by two transpose reads: for
     // read s (slots 4s..4s+3) lane l points at key 4*lh + (l % 16) / 4 + 8s of
@@ -230,11 +175,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 #pragma unroll
     for (int tt = 0; tt < D / 32; ++tt)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int key = 4 * lh + (lane % 16) / 4 + 8 * s;
-            const int d0 = tt * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
-            v_off[tt][s] = vbase + key * TL::kRowBytes + (((d0 / 8) ^ TL::swz(key)) * 16) + (d0 % 8) * 2;
-        }
+        for (int s = 0; s < 2; ++s) v_off[tt][s] = vbase + TL::tr_offset(tt, s, lane);
 
     // S^T tile of 64 keys from the K tile in ring slot `slot`: K fragment
     // i = st * (D/16) + c is key row st*32 + li, d slice c*16 + lh*8.

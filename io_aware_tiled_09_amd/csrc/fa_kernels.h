@@ -16,5 +16,11 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, flo
                        int BH, int N, int d, float scale_log2, bool causal, hipStream_t stream);
 hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                       int BH, int N, int d, float scale_log2, bool causal, hipStream_t stream);
+// Backward pass (bf16 tensors, fp32 lse); delta: BH*N floats of workspace.
+// scale_log2 as above; scale = the softmax scale itself (>= 0).
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* delta, int BH, int N, int d, float scale_log2, float scale,
+                           bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -33,7 +33,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "sample_rows", "useful_flops"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_dout", "sample_rows", "useful_flops",
+           "backward_flops"]
 
 
 @dataclass(frozen=True)
@@ -134,6 +135,24 @@ def make_qkv(w: Workload | str | None = None, *, B=None, H=None, N=None, d=None,
     return _cast(q, w.dtype), _cast(k, w.dtype), _cast(v, w.dtype)
 
 
+def make_dout(w: Workload | str | None = None, *, B=None, H=None, N=None, d=None,
+              dtype=None, seed=None):
+    """Upstream gradient dO for the backward pass: a contiguous CPU tensor of
+    shape [B, H, N, d] with i.i.d. N(0, 1) fp32 entries cast to the storage
+    dtype, drawn from its own generator seeded with ``seed + 500009`` so that
+    it is independent of the workload's Q, K and V draws."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if w is not None:
+        B, H, N, d = (w.B if B is None else B, w.H if H is None else H,
+                      w.N if N is None else N, w.d if d is None else d)
+        dtype = dtype or w.dtype
+        seed = w.seed if seed is None else seed
+    g = torch.Generator(device="cpu").manual_seed(int(seed or 0) + 500009)
+    x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    return _cast(x, dtype or "bf16")
+
+
 def sample_rows(N: int, count: int, seed: int, heads: int = 1) -> torch.Tensor:
     """Seeded, sorted sample of ``count`` distinct query rows per head.
 
@@ -159,4 +178,13 @@ def useful_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     """Useful FLOPs of one forward call: 2*N*N*d for QK^T plus 2*N*N*d for PV
     per head, halved when causal (only keys j <= i count)."""
     f = 4.0 * B * H * N * N * d
+    return f / 2.0 if causal else f
+
+
+def backward_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Useful FLOPs of one backward call: the five N x N x d products
+    S = Q K^T (recomputed), dP = dO V^T, dV = P^T dO, dQ = dS K and
+    dK = dS^T Q, 2*N*N*d each per head, halved when causal; i.e. 2.5 times
+    the forward's useful FLOPs."""
+    f = 10.0 * B * H * N * N * d
     return f / 2.0 if causal else f

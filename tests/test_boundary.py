@@ -80,3 +80,26 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "libfa.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _binding.fa_fwd(A, A, A, A, A, 1, 1, 1, 64, 1.0, 0)
+
+
+def _bwd(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+         dout=A + 320 * MB, dq=A + 384 * MB, dk=A + 448 * MB, dv=A + 512 * MB, ws=A + 576 * MB,
+         B=1, H=2, N=100, d=64, scale=0.125, causal=0):
+    return fa.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, d, scale, causal, 0)
+
+
+def test_bwd_argument_errors():
+    assert _bwd(dout=0) == 1
+    assert _bwd(ws=0) == 1
+    assert _bwd(N=-1) == 2
+    assert _bwd(d=32) == 3
+    assert _bwd(scale=float("nan")) == 4
+    assert _bwd(dq=A + 384 * MB + 8) == 5
+    assert _bwd(ws=A + 576 * MB + 2) == 5
+    assert _bwd(dq=A) == 6                        # dq is q
+    assert _bwd(dk=A + 320 * MB + 256) == 6       # dk inside dout
+    assert _bwd(ws=A + 256 * MB) == 6             # workspace is lse
+    assert _bwd(dv=A + 448 * MB) == 6             # dv is dk
+    assert _bwd(B=65536, H=65536, N=128) == 8
+    for B, H, N in ((0, 4, 100), (2, 0, 100), (2, 4, 0)):
+        assert fa.fa_bwd(*([None] * 10), B, H, N, 64, 0.125, 1, None) == 0

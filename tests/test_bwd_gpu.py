@@ -1,0 +1,94 @@
+"""GPU parity of the backward pass (fa_bwd through the C ABI) against the fp64
+backward oracle. The GPU's own forward supplies O and lse, as in training;
+dO is a seeded N(0, 1) draw. Bounds are in tests/_parity.py."""
+import math
+
+import pytest
+import torch
+
+import io_aware_tiled_09_amd as fa
+from io_aware_tiled_09_amd.inputs import WORKLOADS, make_dout, make_qkv, sample_rows
+
+from _parity import (GRAD_SPIKY_MAX_REL, GRAD_SPIKY_MEAN_REL, check_bwd_full, check_bwd_sampled,
+                     run_gpu_bwd, say)
+
+pytestmark = pytest.mark.gpu
+
+TINY_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 257]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", TINY_N)
+def test_bwd_tiny_shapes(N, d, causal):
+    say(f"bwd tiny N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B=1, H=2, N=N, d=d, seed=N * 13 + d)
+    do = make_dout(B=1, H=2, N=N, d=d, seed=N * 13 + d)
+    check_bwd_full(q, k, v, do, causal, 1.0 / math.sqrt(d), f"N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_ragged_multi_block(d, causal):
+    say(f"bwd ragged B=2 H=3 N=333 d={d} causal={causal}")
+    q, k, v = make_qkv(B=2, H=3, N=333, d=d, seed=31 + d)
+    do = make_dout(B=2, H=3, N=333, d=d, seed=31 + d)
+    check_bwd_full(q, k, v, do, causal, 1.0 / math.sqrt(d), "N=333")
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+def test_bwd_explicit_scale(scale):
+    say(f"bwd scale={scale} B=1 H=3 N=300 d=64 causal")
+    q, k, v = make_qkv(B=1, H=3, N=300, d=64, seed=41)
+    do = make_dout(B=1, H=3, N=300, d=64, seed=41)
+    check_bwd_full(q, k, v, do, True, scale, f"scale={scale}")
+
+
+@pytest.mark.parametrize("name", ["bert512", "gpt2_1k", "gpt2_1k_spiky"])
+def test_bwd_workload_heads(name):
+    w = WORKLOADS[name]
+    heads = [0, (w.B * w.H) // 2 + 1, w.B * w.H - 1]
+    say(f"bwd workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}, heads {heads}")
+    q, k, v = make_qkv(w)
+    bounds = {}
+    if w.spike_frac > 0:
+        bounds = dict(max_rel=GRAD_SPIKY_MAX_REL, mean_rel=GRAD_SPIKY_MEAN_REL)
+    check_bwd_full(q, k, v, make_dout(w), w.causal, w.scale, name, heads=heads, **bounds)
+
+
+def test_bwd_longdoc8k_sampled():
+    w = WORKLOADS["longdoc8k"]
+    heads = [0, 37, w.B * w.H - 1]
+    fixed = torch.tensor([0, 63, 64, 127, 128, 255, 256, w.N // 2, w.N - 129, w.N - 2,
+                          w.N - 1], dtype=torch.int64)
+    qrows = torch.cat([sample_rows(w.N, 24, seed=w.seed + 91, heads=len(heads)),
+                       fixed.expand(len(heads), -1)], dim=1)
+    krows = torch.cat([sample_rows(w.N, 24, seed=w.seed + 92, heads=len(heads)),
+                       fixed.expand(len(heads), -1)], dim=1)
+    say(f"bwd workload longdoc8k: B={w.B} H={w.H} N={w.N} d={w.d} causal, heads {heads}, "
+        f"{qrows.shape[1]} query rows and {krows.shape[1]} key rows each")
+    q, k, v = make_qkv(w)
+    check_bwd_sampled(q, k, v, make_dout(w), w.causal, w.scale, heads, qrows, krows,
+                      "longdoc8k")
+
+
+def test_bwd_deterministic_bitwise():
+    say("bwd determinism B=2 H=4 N=1000 d=128 causal")
+    q, k, v = make_qkv(B=2, H=4, N=1000, d=128, seed=7)
+    do = make_dout(B=2, H=4, N=1000, d=128, seed=7)
+    a = run_gpu_bwd(q, k, v, do, True, 1.0 / math.sqrt(128))
+    b = run_gpu_bwd(q, k, v, do, True, 1.0 / math.sqrt(128))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_leaves_inputs_untouched():
+    say("bwd inputs untouched B=1 H=2 N=200 d=64")
+    q, k, v = (t.cuda() for t in make_qkv(B=1, H=2, N=200, d=64, seed=8))
+    do = make_dout(B=1, H=2, N=200, d=64, seed=8).cuda()
+    o, lse = fa.attention(q, k, v, causal=False)
+    before = [t.clone() for t in (q, k, v, o, lse, do)]
+    fa.attention_backward(q, k, v, o, lse, do, causal=False)
+    torch.cuda.synchronize()
+    for x, y in zip(before, (q, k, v, o, lse, do)):
+        assert torch.equal(x, y)

@@ -64,3 +64,23 @@ def test_useful_flops():
     assert useful_flops(2, 32, 8192, 128, True) == 4.0 * 2 * 32 * 8192 ** 2 * 128 / 2
     assert useful_flops(1, 1, 10, 4, False) == 1600.0
     assert isinstance(WORKLOADS["longdoc8k"], Workload)
+
+
+def test_make_dout_is_seeded_and_independent_of_qkv():
+    from io_aware_tiled_09_amd.inputs import make_dout, make_qkv
+    a = make_dout("gpt2_1k", B=1, H=2, N=64)
+    b = make_dout("gpt2_1k", B=1, H=2, N=64)
+    assert a.dtype == torch.bfloat16 and a.shape == (1, 2, 64, 64) and a.is_contiguous()
+    assert torch.equal(a, b)
+    q, k, v = make_qkv("gpt2_1k", B=1, H=2, N=64)
+    assert not any(torch.equal(a, t) for t in (q, k, v))
+    c = make_dout(B=1, H=1, N=3, d=64, seed=1, dtype="fp32")
+    assert c.dtype == torch.float32 and not torch.equal(c, make_dout(B=1, H=1, N=3, d=64, seed=2,
+                                                                      dtype="fp32"))
+
+
+def test_backward_flops_is_two_and_a_half_forwards():
+    from io_aware_tiled_09_amd.inputs import backward_flops, useful_flops
+    for causal in (False, True):
+        assert backward_flops(2, 32, 8192, 128, causal) == 2.5 * useful_flops(2, 32, 8192, 128,
+                                                                               causal)
