@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_lds.h"
 
@@ -92,38 +94,57 @@ __device__ inline void issue_tile(const __bf16* src, int t, int N, unsigned char
 
 // Rows of a partial last tile past the sequence end are cleared once the
 // tile has landed: their weights are 0, and 0 * NaN would leak.
-template <typename TL>
+template <typename TL, int THREADS = kBwdThreads>
 __device__ inline void clear_tile_tail(int t, int N, unsigned char* dst, int tid)
 {
     const int rows = N - t * kBc;
     if (rows >= kBc) return;
-    for (int x = tid; x < (kBc - rows) * TL::kChunks; x += kBwdThreads) {
+    for (int x = tid; x < (kBc - rows) * TL::kChunks; x += THREADS) {
         const int row = rows + x / TL::kChunks;
         *reinterpret_cast<bf16x8*>(dst + row * TL::kRowBytes + (x % TL::kChunks) * 16) = bf16x8{};
     }
 }
 
 // ---------------------------------------------------------------- dk, dv
+// One workgroup per 128 keys of a head: 4 key groups of 32, each served by a
+// pair of waves that share the work of every 64-query tile:
+//  * the P-wave keeps its keys' K rows as B operands, forms S = Q K^T and
+//    P = exp2(S c - lse2), hands P (bf16) to its partner through LDS, and
+//    accumulates dV^T += dO^T P;
+//  * the dS-wave keeps the V rows, forms dP = dO V^T, takes P, forms
+//    dS = P (dP - D) and accumulates dK^T += Q^T dS.
+// Each wave then holds one 32x128 accumulator and one operand set (about half
+// the registers of a wave doing both), so two waves fit per SIMD; waves w and
+// w + 4 share a SIMD and serve different key groups, so one's softmax work
+// overlaps the other's MFMAs. The four products are split evenly.
+constexpr int kDkdvWaves = 8;
+constexpr int kDkdvThreads = kDkdvWaves * 64;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                         const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                         const float* __restrict__ lse, const float* __restrict__ delta,
                         __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH, int N,
                         int nkblk, float scale_log2, float scale)
 {
-    using TL = Tile<D, kBwdWaves>;
+    using TL = Tile<D, kDkdvWaves>;
     constexpr int L = TL::kLoadsPerWave;
     __shared__ __attribute__((aligned(1024))) unsigned char qbuf[2][TL::kBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char dobuf[2][TL::kBytes];
     __shared__ __attribute__((aligned(16))) float lse_s[2][kBc];  // lse * log2(e) per query
     __shared__ __attribute__((aligned(16))) float dl_s[2][kBc];   // D per query
+    // P of the current tile per key group: [group][sub-tile][half][lane] x 8 bf16
+    // (lane-major 16-byte slots, conflict-free).
+    __shared__ __attribute__((aligned(16))) bf16x8 p_x[kBwdWaves][kBc / 32][2][64];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int li = lane & 31;
     const int lh = lane >> 5;
+    const bool pwave = wave < kBwdWaves;                     // forms P, accumulates dV
+    const int grp = pwave ? wave : (wave + kBwdWaves - 1) % kBwdWaves;
 
     // Key blocks in ascending order: for causal attention the first key
     // blocks see the most queries, so the heaviest work starts first.
@@ -136,19 +157,16 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     const float* dlh = delta + (size_t)bh * N;
 
     const int k0 = kblk * kBwdRows;
-    const int kw0 = k0 + wave * 32;   // first key of this wave
+    const int kw0 = k0 + grp * 32;    // first key of this wave's group
     const int kj = kw0 + li;          // this lane's key
 
-    // K and V rows of this lane's key as B operands (8 d values per lane).
-    bf16x8 kf[D / 16], vf[D / 16];
+    // K rows (P-wave) or V rows (dS-wave) of this lane's key as B operands.
+    bf16x8 bf[D / 16];
     {
-        const __bf16* krow = k + head_off + (size_t)kj * D;
-        const __bf16* vrow = v + head_off + (size_t)kj * D;
+        const __bf16* row = (pwave ? k : v) + head_off + (size_t)kj * D;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            kf[c] = kj < N ? *reinterpret_cast<const bf16x8*>(krow + c * 16 + lh * 8) : bf16x8{};
-            vf[c] = kj < N ? *reinterpret_cast<const bf16x8*>(vrow + c * 16 + lh * 8) : bf16x8{};
-        }
+        for (int c = 0; c < D / 16; ++c)
+            bf[c] = kj < N ? *reinterpret_cast<const bf16x8*>(row + c * 16 + lh * 8) : bf16x8{};
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
@@ -180,20 +198,17 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         else if (tid < 2 * kBc) dl_s[t & 1][tid - kBc] = x;
     };
 
-    f32x16 acc_k[D / 32], acc_v[D / 32];
+    f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (dS-wave): rows d, column = key
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-        acc_k[t] = f32x16{};
-        acc_v[t] = f32x16{};
-    }
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
     if (t0 < nqt) {
         issue_tile<TL>(qh, t0, N, qbuf[t0 & 1], ld_off, wave);
         issue_tile<TL>(doh, t0, N, dobuf[t0 & 1], ld_off, wave);
         put_stats(t0, fetch_stats(t0));
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-        clear_tile_tail<TL>(t0, N, qbuf[t0 & 1], tid);
-        clear_tile_tail<TL>(t0, N, dobuf[t0 & 1], tid);
+        clear_tile_tail<TL, kDkdvThreads>(t0, N, qbuf[t0 & 1], tid);
+        clear_tile_tail<TL, kDkdvThreads>(t0, N, dobuf[t0 & 1], tid);
         __syncthreads();
     }
 
@@ -205,52 +220,82 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             issue_tile<TL>(doh, t + 1, N, dobuf[b ^ 1], ld_off, wave);
             next_stats = fetch_stats(t + 1);
         }
-        // Causal: a wave whose keys all follow every query of the tile skips it.
+        // Causal: a group whose keys all follow every query of the tile skips it.
         const bool active = !CAUSAL || t * kBc + kBc - 1 >= kw0;
+        const bool need_mask = (CAUSAL && t * kBc < kw0 + 31) || t * kBc + kBc > N;
+        const unsigned char* qt = qbuf[b];
+        const unsigned char* dt = dobuf[b];
+        // S (P-wave, from Q) or dP (dS-wave, from dO) for the tile's 64
+        // queries: lane = key, 16 queries per 32-query sub-tile.
+        f32x16 x[kBc / 32];
+        bf16x8 pf[kBc / 32][2];
         if (active) {
-            const unsigned char* qt = qbuf[b];
-            const unsigned char* dt = dobuf[b];
-            // S = Q K^T and dP = dO V^T for the tile's 64 queries: lane = key,
-            // 16 queries per 32-query sub-tile.
-            f32x16 s[kBc / 32], dp[kBc / 32];
+            const unsigned char* at = pwave ? qt : dt;
 #pragma unroll
             for (int st = 0; st < kBc / 32; ++st) {
-                s[st] = f32x16{};
-                dp[st] = f32x16{};
+                x[st] = f32x16{};
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    const int off = st * 32 * TL::kRowBytes + f_off[c];
-                    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + off);
-                    const bf16x8 da = *reinterpret_cast<const bf16x8*>(dt + off);
-                    s[st] = mfma(qa, kf[c], s[st]);
-                    dp[st] = mfma(da, vf[c], dp[st]);
-                }
+                for (int c = 0; c < D / 16; ++c)
+                    x[st] = mfma(*reinterpret_cast<const bf16x8*>(at + st * 32 * TL::kRowBytes +
+                                                                  f_off[c]),
+                                 bf[c], x[st]);
             }
-            // P = exp2(s c - lse2_q) (0 where masked), dS = P (dP - D_q).
-            const bool need_mask = (CAUSAL && t * kBc < kw0 + 31) || t * kBc + kBc > N;
-            bf16x8 pf[kBc / 32][2], dsf[kBc / 32][2];
+            if (pwave) {
+                // P = exp2(s c - lse2_q), 0 where masked; published for the
+                // partner. Query qloc + i of the tile is valid for this lane's
+                // key iff lo <= qloc + i < hi (one unsigned compare); tiles
+                // that need no mask take a separate path without it.
+                const int lo = CAUSAL ? kj - t * kBc : 0;
+                const int hi = N - t * kBc;
+                auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-            for (int st = 0; st < kBc / 32; ++st)
+                    for (int st = 0; st < kBc / 32; ++st) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int qloc = st * 32 + g * 8 + lh * 4;  // queries qloc .. qloc+3
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][qloc]);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_s[b][qloc]);
+                        for (int g = 0; g < 4; ++g) {
+                            const int qloc = st * 32 + g * 8 + lh * 4;  // queries qloc .. qloc+3
+                            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][qloc]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = g * 4 + i;
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], scale_log2, -l4[i]));
-                        if (need_mask) {
-                            const int qq = t * kBc + qloc + i;
-                            const bool ok = qq < N && (!CAUSAL || qq >= kj);
-                            p = ok ? p : 0.f;
+                            for (int i = 0; i < 4; ++i) {
+                                const int r = g * 4 + i;
+                                float p = __builtin_amdgcn_exp2f(
+                                    __builtin_fmaf(x[st][r], scale_log2, -l4[i]));
+                                if constexpr (decltype(masked)::value)
+                                    p = (unsigned)(qloc + i - lo) < (unsigned)(hi - lo) ? p : 0.f;
+                                pf[st][r >> 3][r & 7] = (__bf16)p;
+                            }
                         }
-                        const float ds = p * (dp[st][r] - d4[i]);
-                        pf[st][r >> 3][r & 7] = (__bf16)p;
-                        dsf[st][r >> 3][r & 7] = (__bf16)ds;
+                        p_x[grp][st][0][lane] = pf[st][0];
+                        p_x[grp][st][1][lane] = pf[st][1];
+                    }
+                };
+                if (need_mask) probs(std::true_type{});
+                else probs(std::false_type{});
+            }
+        }
+        __syncthreads();  // P of every group is in LDS
+        if (active) {
+            if (!pwave) {
+                // dS = P (dP - D_q), P from the partner.
+#pragma unroll
+                for (int st = 0; st < kBc / 32; ++st) {
+                    const bf16x8 p0 = p_x[grp][st][0][lane];
+                    const bf16x8 p1 = p_x[grp][st][1][lane];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int qloc = st * 32 + g * 8 + lh * 4;
+                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_s[b][qloc]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = g * 4 + i;
+                            const float p = (float)(r < 8 ? p0[r & 7] : p1[r & 7]);
+                            pf[st][r >> 3][r & 7] = (__bf16)(p * (x[st][r] - d4[i]));
+                        }
                     }
                 }
-            // dV^T += dO^T P and dK^T += Q^T dS, A operands by transpose reads.
+            }
+            // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave); A operands by
+            // transpose reads of the dO or Q tile.
+            const unsigned char* tt_base = pwave ? dt : qt;
 #pragma unroll
             for (int tt = 0; tt < D / 32; ++tt)
 #pragma unroll
@@ -258,34 +303,28 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const int base = (st * 32 + h2 * 16) * TL::kRowBytes;
-                        const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(dt + base + t_off[tt][0]));
-                        const s16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(dt + base + t_off[tt][1]));
-                        const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(qt + base + t_off[tt][0]));
-                        const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(qt + base + t_off[tt][1]));
-                        const s16x4 dpair[2] = {dlo, dhi}, qpair[2] = {qlo, qhi};
-                        bf16x8 da, qa;
-                        __builtin_memcpy(&da, dpair, sizeof(da));
-                        __builtin_memcpy(&qa, qpair, sizeof(qa));
-                        acc_v[tt] = mfma(da, pf[st][h2], acc_v[tt]);
-                        acc_k[tt] = mfma(qa, dsf[st][h2], acc_k[tt]);
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(tt_base + base + t_off[tt][0]));
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(tt_base + base + t_off[tt][1]));
+                        const s16x4 pair[2] = {lo, hi};
+                        bf16x8 a;
+                        __builtin_memcpy(&a, pair, sizeof(a));
+                        acc[tt] = mfma(a, pf[st][h2], acc[tt]);
                     }
         }
         if (t + 1 < nqt) {
             __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // this wave's loads of tile t+1
-            clear_tile_tail<TL>(t + 1, N, qbuf[b ^ 1], tid);
-            clear_tile_tail<TL>(t + 1, N, dobuf[b ^ 1], tid);
+            clear_tile_tail<TL, kDkdvThreads>(t + 1, N, qbuf[b ^ 1], tid);
+            clear_tile_tail<TL, kDkdvThreads>(t + 1, N, dobuf[b ^ 1], tid);
             put_stats(t + 1, next_stats);
         }
         __syncthreads();
     }
 
     if (kj < N) {
-        store_row<D>(dk + head_off + (size_t)kj * D, acc_k, scale, lh);
-        store_row<D>(dv + head_off + (size_t)kj * D, acc_v, 1.0f, lh);
+        if (pwave) store_row<D>(dv + head_off + (size_t)kj * D, acc, 1.0f, lh);
+        else store_row<D>(dk + head_off + (size_t)kj * D, acc, scale, lh);
     }
 }
 
@@ -439,7 +478,7 @@ hipError_t launch_bwd_one(const __bf16* q, const __bf16* k, const __bf16* v, con
                        stream, o, dout, delta, rows);
     const int nblk = (N + kBwdRows - 1) / kBwdRows;
     const dim3 grid((unsigned)((long long)BH * nblk));
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, q, k,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(kDkdvThreads), 0, stream, q, k,
                        v, dout, lse, delta, dk, dv, BH, N, nblk, scale_log2, scale);
     hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, q, k, v,
                        dout, lse, delta, dq, BH, N, nblk, scale_log2, scale);
