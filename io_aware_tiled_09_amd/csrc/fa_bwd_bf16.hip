@@ -113,10 +113,15 @@ __device__ inline void clear_tile_tail(int t, int N, unsigned char* dst, int tid
 //    accumulates dV^T += dO^T P;
 //  * the dS-wave keeps the V rows, forms dP = dO V^T, takes P, forms
 //    dS = P (dP - D) and accumulates dK^T += Q^T dS.
-// Each wave then holds one 32x128 accumulator and one operand set (about half
-// the registers of a wave doing both), so two waves fit per SIMD; waves w and
-// w + 4 share a SIMD and serve different key groups, so one's softmax work
-// overlaps the other's MFMAs. The four products are split evenly.
+// Each wave holds one 32x128 accumulator and one operand set (about half the
+// registers of a wave doing both), so two waves fit per SIMD; waves w and
+// w + 4 share a SIMD and serve different key groups.
+// The pair is software-pipelined by one tile: in step t the P-wave does
+// dV(t) then S(t+1), P(t+1), and the dS-wave does dS(t), dK(t) then dP(t+1).
+// Each wave's MFMA runs then sit next to the other wave's VALU work
+// (exponentials at the P-wave's end, dS at the dS-wave's start), and one
+// barrier per tile publishes both P(t+1) and the next Q/dO tile. Q and dO
+// tiles use three LDS buffers (t, t+1 in use, t+2 loading), P two.
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * 64;
 
@@ -130,13 +135,13 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 {
     using TL = Tile<D, kDkdvWaves>;
     constexpr int L = TL::kLoadsPerWave;
-    __shared__ __attribute__((aligned(1024))) unsigned char qbuf[2][TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char dobuf[2][TL::kBytes];
-    __shared__ __attribute__((aligned(16))) float lse_s[2][kBc];  // lse * log2(e) per query
-    __shared__ __attribute__((aligned(16))) float dl_s[2][kBc];   // D per query
-    // P of the current tile per key group: [group][sub-tile][half][lane] x 8 bf16
-    // (lane-major 16-byte slots, conflict-free).
-    __shared__ __attribute__((aligned(16))) bf16x8 p_x[kBwdWaves][kBc / 32][2][64];
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf[3][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char dobuf[3][TL::kBytes];
+    __shared__ __attribute__((aligned(16))) float lse_s[3][kBc];  // lse * log2(e) per query
+    __shared__ __attribute__((aligned(16))) float dl_s[3][kBc];   // D per query
+    // P of a tile per key group: [tile & 1][group][sub-tile][half][lane] x 8
+    // bf16 (lane-major 16-byte slots, conflict-free).
+    __shared__ __attribute__((aligned(16))) bf16x8 p_x[2][kBwdWaves][kBc / 32][2][64];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -185,141 +190,161 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     const int nqt = (N + kBc - 1) / kBc;
     // Causal: query tiles before the block's first key see none of its keys.
     const int t0 = CAUSAL ? k0 / kBc : 0;
+    if (t0 >= nqt) return;  // uniform over the workgroup: no barrier is skipped
+    // Tiles where some (query, key) pair of the group is invalid: the causal
+    // diagonal (including the first tile, whose queries may all precede a
+    // group's keys; there every P is 0) and the sequence tail.
+    auto need_mask = [&](int u) __attribute__((always_inline)) {
+        return (CAUSAL && u * kBc < kw0 + 31) || u * kBc + kBc > N;
+    };
 
-    // Per-query statistics of tile t: threads 0..63 fetch lse, 64..127 D.
-    auto fetch_stats = [&](int t) __attribute__((always_inline)) {
-        const int qq = t * kBc + (tid & 63);
+    // Per-query statistics of tile u: threads 0..63 fetch lse, 64..127 D.
+    auto fetch_stats = [&](int u) __attribute__((always_inline)) {
+        const int qq = u * kBc + (tid & 63);
         float x = 0.f;
         if (tid < 2 * kBc && qq < N) x = tid < kBc ? lseh[qq] * kLog2e : dlh[qq];
         return x;
     };
-    auto put_stats = [&](int t, float x) __attribute__((always_inline)) {
-        if (tid < kBc) lse_s[t & 1][tid] = x;
-        else if (tid < 2 * kBc) dl_s[t & 1][tid - kBc] = x;
+    auto put_stats = [&](int u, float x) __attribute__((always_inline)) {
+        if (tid < kBc) lse_s[u % 3][tid] = x;
+        else if (tid < 2 * kBc) dl_s[u % 3][tid - kBc] = x;
+    };
+    auto load_tile = [&](int u) __attribute__((always_inline)) {
+        issue_tile<TL>(qh, u, N, qbuf[u % 3], ld_off, wave);
+        issue_tile<TL>(doh, u, N, dobuf[u % 3], ld_off, wave);
+    };
+    auto clear_tails = [&](int u) __attribute__((always_inline)) {
+        clear_tile_tail<TL, kDkdvThreads>(u, N, qbuf[u % 3], tid);
+        clear_tile_tail<TL, kDkdvThreads>(u, N, dobuf[u % 3], tid);
     };
 
-    f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (dS-wave): rows d, column = key
+    // S (P-wave, from Q) or dP (dS-wave, from dO) of tile u: lane = key, 16
+    // queries per 32-query sub-tile.
+    f32x16 x[kBc / 32];
+    auto scores = [&](int u) __attribute__((always_inline)) {
+        const unsigned char* at = pwave ? qbuf[u % 3] : dobuf[u % 3];
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-
-    if (t0 < nqt) {
-        issue_tile<TL>(qh, t0, N, qbuf[t0 & 1], ld_off, wave);
-        issue_tile<TL>(doh, t0, N, dobuf[t0 & 1], ld_off, wave);
-        put_stats(t0, fetch_stats(t0));
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-        clear_tile_tail<TL, kDkdvThreads>(t0, N, qbuf[t0 & 1], tid);
-        clear_tile_tail<TL, kDkdvThreads>(t0, N, dobuf[t0 & 1], tid);
-        __syncthreads();
-    }
-
-    for (int t = t0; t < nqt; ++t) {
-        const int b = t & 1;
-        float next_stats = 0.f;
-        if (t + 1 < nqt) {
-            issue_tile<TL>(qh, t + 1, N, qbuf[b ^ 1], ld_off, wave);
-            issue_tile<TL>(doh, t + 1, N, dobuf[b ^ 1], ld_off, wave);
-            next_stats = fetch_stats(t + 1);
+        for (int st = 0; st < kBc / 32; ++st) {
+            x[st] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+                x[st] = mfma(*reinterpret_cast<const bf16x8*>(at + st * 32 * TL::kRowBytes +
+                                                              f_off[c]),
+                             bf[c], x[st]);
         }
-        // Causal: a group whose keys all follow every query of the tile skips it.
-        const bool active = !CAUSAL || t * kBc + kBc - 1 >= kw0;
-        const bool need_mask = (CAUSAL && t * kBc < kw0 + 31) || t * kBc + kBc > N;
-        const unsigned char* qt = qbuf[b];
-        const unsigned char* dt = dobuf[b];
-        // S (P-wave, from Q) or dP (dS-wave, from dO) for the tile's 64
-        // queries: lane = key, 16 queries per 32-query sub-tile.
-        f32x16 x[kBc / 32];
-        bf16x8 pf[kBc / 32][2];
-        if (active) {
-            const unsigned char* at = pwave ? qt : dt;
+    };
+    // P-wave: P = exp2(s c - lse2_q) of tile u, 0 where masked, into pf and
+    // p_x[u & 1]. Query qloc + i of the tile is valid for this lane's key iff
+    // lo <= qloc + i < hi (one unsigned compare); tiles that need no mask
+    // take a separate path without it.
+    bf16x8 pf[kBc / 32][2];
+    auto probs = [&](int u) __attribute__((always_inline)) {
+        const int lo = CAUSAL ? kj - u * kBc : 0;
+        const int hi = N - u * kBc;
+        const float* ls = lse_s[u % 3];
+        auto run = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
             for (int st = 0; st < kBc / 32; ++st) {
-                x[st] = f32x16{};
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c)
-                    x[st] = mfma(*reinterpret_cast<const bf16x8*>(at + st * 32 * TL::kRowBytes +
-                                                                  f_off[c]),
-                                 bf[c], x[st]);
-            }
-            if (pwave) {
-                // P = exp2(s c - lse2_q), 0 where masked; published for the
-                // partner. Query qloc + i of the tile is valid for this lane's
-                // key iff lo <= qloc + i < hi (one unsigned compare); tiles
-                // that need no mask take a separate path without it.
-                const int lo = CAUSAL ? kj - t * kBc : 0;
-                const int hi = N - t * kBc;
-                auto probs = [&](auto masked) __attribute__((always_inline)) {
+                for (int g = 0; g < 4; ++g) {
+                    const int qloc = st * 32 + g * 8 + lh * 4;  // queries qloc .. qloc+3
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&ls[qloc]);
 #pragma unroll
-                    for (int st = 0; st < kBc / 32; ++st) {
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int qloc = st * 32 + g * 8 + lh * 4;  // queries qloc .. qloc+3
-                            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][qloc]);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int r = g * 4 + i;
-                                float p = __builtin_amdgcn_exp2f(
-                                    __builtin_fmaf(x[st][r], scale_log2, -l4[i]));
-                                if constexpr (decltype(masked)::value)
-                                    p = (unsigned)(qloc + i - lo) < (unsigned)(hi - lo) ? p : 0.f;
-                                pf[st][r >> 3][r & 7] = (__bf16)p;
-                            }
-                        }
-                        p_x[grp][st][0][lane] = pf[st][0];
-                        p_x[grp][st][1][lane] = pf[st][1];
-                    }
-                };
-                if (need_mask) probs(std::true_type{});
-                else probs(std::false_type{});
-            }
-        }
-        __syncthreads();  // P of every group is in LDS
-        if (active) {
-            if (!pwave) {
-                // dS = P (dP - D_q), P from the partner.
-#pragma unroll
-                for (int st = 0; st < kBc / 32; ++st) {
-                    const bf16x8 p0 = p_x[grp][st][0][lane];
-                    const bf16x8 p1 = p_x[grp][st][1][lane];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int qloc = st * 32 + g * 8 + lh * 4;
-                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_s[b][qloc]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = g * 4 + i;
-                            const float p = (float)(r < 8 ? p0[r & 7] : p1[r & 7]);
-                            pf[st][r >> 3][r & 7] = (__bf16)(p * (x[st][r] - d4[i]));
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = g * 4 + i;
+                        float p = __builtin_amdgcn_exp2f(
+                            __builtin_fmaf(x[st][r], scale_log2, -l4[i]));
+                        if constexpr (decltype(masked)::value)
+                            p = (unsigned)(qloc + i - lo) < (unsigned)(hi - lo) ? p : 0.f;
+                        pf[st][r >> 3][r & 7] = (__bf16)p;
                     }
                 }
+                p_x[u & 1][grp][st][0][lane] = pf[st][0];
+                p_x[u & 1][grp][st][1][lane] = pf[st][1];
             }
-            // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave); A operands by
-            // transpose reads of the dO or Q tile.
-            const unsigned char* tt_base = pwave ? dt : qt;
+        };
+        if (need_mask(u)) run(std::true_type{});
+        else run(std::false_type{});
+    };
+    // dS-wave: dS = P (dP - D_q) of tile u into pf, P from the partner.
+    auto dscores = [&](int u) __attribute__((always_inline)) {
+        const float* ds_ = dl_s[u % 3];
 #pragma unroll
-            for (int tt = 0; tt < D / 32; ++tt)
+        for (int st = 0; st < kBc / 32; ++st) {
+            const bf16x8 p0 = p_x[u & 1][grp][st][0][lane];
+            const bf16x8 p1 = p_x[u & 1][grp][st][1][lane];
 #pragma unroll
-                for (int st = 0; st < kBc / 32; ++st)
+            for (int g = 0; g < 4; ++g) {
+                const int qloc = st * 32 + g * 8 + lh * 4;
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ds_[qloc]);
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int base = (st * 32 + h2 * 16) * TL::kRowBytes;
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(tt_base + base + t_off[tt][0]));
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(tt_base + base + t_off[tt][1]));
-                        const s16x4 pair[2] = {lo, hi};
-                        bf16x8 a;
-                        __builtin_memcpy(&a, pair, sizeof(a));
-                        acc[tt] = mfma(a, pf[st][h2], acc[tt]);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int r = g * 4 + i;
+                    const float p = (float)(r < 8 ? p0[r & 7] : p1[r & 7]);
+                    pf[st][r >> 3][r & 7] = (__bf16)(p * (x[st][r] - d4[i]));
+                }
+            }
         }
-        if (t + 1 < nqt) {
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // this wave's loads of tile t+1
-            clear_tile_tail<TL, kDkdvThreads>(t + 1, N, qbuf[b ^ 1], tid);
-            clear_tile_tail<TL, kDkdvThreads>(t + 1, N, dobuf[b ^ 1], tid);
-            put_stats(t + 1, next_stats);
-        }
+    };
+    f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (dS-wave): rows d, column = key
+#pragma unroll
+    for (int tt = 0; tt < D / 32; ++tt) acc[tt] = f32x16{};
+    // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave) for tile u, A
+    // operands by transpose reads of the dO or Q tile.
+    auto accumulate = [&](int u) __attribute__((always_inline)) {
+        const unsigned char* tb = pwave ? dobuf[u % 3] : qbuf[u % 3];
+#pragma unroll
+        for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+            for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int base = (st * 32 + h2 * 16) * TL::kRowBytes;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(tb + base + t_off[tt][0]));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(tb + base + t_off[tt][1]));
+                    const s16x4 pair[2] = {lo, hi};
+                    bf16x8 a;
+                    __builtin_memcpy(&a, pair, sizeof(a));
+                    acc[tt] = mfma(a, pf[st][h2], acc[tt]);
+                }
+    };
+
+    // Prologue: tiles t0 and t0 + 1 resident, then S/P or dP of tile t0.
+    load_tile(t0);
+    if (t0 + 1 < nqt) load_tile(t0 + 1);
+    put_stats(t0, fetch_stats(t0));
+    if (t0 + 1 < nqt) put_stats(t0 + 1, fetch_stats(t0 + 1));
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    clear_tails(t0);
+    if (t0 + 1 < nqt) clear_tails(t0 + 1);
+    __syncthreads();
+    scores(t0);
+    if (pwave) probs(t0);
+
+    // Step t: the dS-wave forms dS(t); both accumulate tile t (dV or dK);
+    // both form the scores of tile t + 1 (S or dP) and the P-wave P(t+1).
+    for (int t = t0; t < nqt; ++t) {
+        // P(t) and tile t + 1 are visible after this barrier; tile t - 1's
+        // buffers and P(t - 1) are no longer read.
         __syncthreads();
+        float next_stats = 0.f;
+        if (t + 2 < nqt) {
+            load_tile(t + 2);
+            next_stats = fetch_stats(t + 2);
+        }
+        if (!pwave) dscores(t);
+        accumulate(t);
+        if (t + 1 < nqt) {
+            scores(t + 1);
+            if (pwave) probs(t + 1);
+        }
+        if (t + 2 < nqt) {
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // this wave's loads of tile t+2
+            clear_tails(t + 2);
+            put_stats(t + 2, next_stats);
+        }
     }
 
     if (kj < N) {
