@@ -13,6 +13,12 @@ launched on (torch's current stream, which the binding passes to fa_fwd).
 The CPU baseline times the fp64 oracle on a bounded sample (whole heads of
 the same workload) on this host's cores.
 
+With --pass std one step is the standard, materializing forward
+(libfa_std.so: S = scale QK^T to HBM by rocBLAS, the row softmax kernel,
+O = PV by rocBLAS) on the same workload; `value` counts the same useful
+FLOPs as the flash forward, and the roofline object is the softmax kernel's
+(HBM-bound: visible fp32 scores read, bf16 P written).
+
 With --pass bwd one step is one backward call (fa_bwd: the D, dK/dV and dQ
 kernels) on the same workload with a seeded N(0,1) dO, O and lse from one
 forward call made before timing; `value` is useful backward TFLOP/s
@@ -35,14 +41,17 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k.json"),
-                 "bwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_bwd.json")}
+                 "bwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_bwd.json"),
+                 "std": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_std.json")}
 # Sources each pass's kernels are compiled from (the traffic summary is valid
 # only for the exact sources it was taken on).
 PASS_SOURCES = {"fwd": ("fa_common.h", "fa_lds.h", "fa_fwd_bf16.hip"),
-                "bwd": ("fa_common.h", "fa_lds.h", "fa_bwd_bf16.hip")}
+                "bwd": ("fa_common.h", "fa_lds.h", "fa_bwd_bf16.hip"),
+                "std": ("fa_common.h", "fa_std.hip")}
 # Kernel names (substrings) rocprofv3 reports for each pass.
 PASS_KERNELS = {"fwd": ("fa_fwd_bf16_kernel",),
-                "bwd": ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel")}
+                "bwd": ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"),
+                "std": ("fa_std_softmax_kernel",)}
 
 
 def log(*a):
@@ -187,9 +196,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="longdoc8k")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "std"), default="fwd",
                     help="fwd: one step = one forward call (the default line); bwd: one "
-                         "step = one backward call (fa_bwd) given O and lse")
+                         "step = one backward call (fa_bwd) given O and lse; std: one step = "
+                         "the standard materializing forward (S and P through HBM)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
@@ -239,7 +249,33 @@ def main(argv=None):
         if st != 0:
             raise fa.FAError(st)
 
-    if bwd:
+    stdp = args.pass_ == "std"
+    std_sm = None  # (start, end) event pairs around the softmax launches
+    if stdp:
+        from io_aware_tiled_09_amd import standard as stdlib
+        need = stdlib.fa_std_workspace_bytes(w.B, w.H, w.N)
+        ws8 = torch.empty(need, dtype=torch.uint8, device=dev)
+        nn = w.B * w.H * w.N * w.N
+        s_buf = ws8[: nn * 4].view(torch.float32)
+        p_off = (nn * 4 + 255) // 256 * 256
+        p_buf = ws8[p_off: p_off + nn * 2].view(torch.bfloat16)
+        g_off = p_off + (nn * 2 + 255) // 256 * 256
+        gws = ws8[g_off:]
+        std_sm = []
+
+        def step(sm_events=None):
+            st = stdlib.fa_std_scores(dq, dk, s_buf, gws, w.B, w.H, w.N, w.d, w.scale, stream)
+            if st == 0:
+                if sm_events is not None:
+                    sm_events[0].record(stream)
+                st = stdlib.fa_std_softmax(s_buf, p_buf, lse, w.B, w.H, w.N, w.causal, stream)
+                if sm_events is not None:
+                    sm_events[1].record(stream)
+            if st == 0:
+                st = stdlib.fa_std_output(p_buf, dv, o, gws, w.B, w.H, w.N, w.d, stream)
+            if st != 0:
+                raise fa.FAError(st)
+    elif bwd:
         do_cpu = make_dout(w)
         ddo = do_cpu.to(dev)
         gq, gk, gv = torch.empty_like(dq), torch.empty_like(dq), torch.empty_like(dq)
@@ -265,7 +301,12 @@ def main(argv=None):
     t0 = time.perf_counter()
     for i in range(K):
         starts[i].record(stream)
-        step()
+        if stdp:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            std_sm.append(ev)
+            step(ev)
+        else:
+            step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -277,6 +318,15 @@ def main(argv=None):
     ms_per_step = max(span_ms, 1e-9) / K
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    if stdp:
+        # Dominant kernel: the softmax over the stored scores, HBM-bound.
+        # Algorithmic bytes per launch: the visible scores read once (fp32),
+        # all of P written once (bf16), lse written (fp32).
+        sm_ms = sum(a.elapsed_time(b) for a, b in std_sm) / K
+        vis = w.N * (w.N + 1) // 2 if w.causal else w.N * w.N
+        sm_bytes = w.B * w.H * (vis * 4 + w.N * w.N * 2 + w.N * 4)
+        sm_gbs = sm_bytes / (sm_ms * 1e-3) / 1e9
+        log(f"softmax launch {sm_ms:.4f} ms, {sm_bytes / 1e9:.3f} GB -> {sm_gbs:.0f} GB/s")
     log(f"avg launch {avg_launch_ms:.4f} ms, median {med_launch_ms:.4f} ms, span/step "
         f"{ms_per_step:.4f} ms, wall/step {wall / K * 1e3:.4f} ms -> {value:.1f} TFLOP/s")
 
@@ -295,6 +345,9 @@ def main(argv=None):
     if bwd:
         metric = ("attention bwd TFLOP/s (bf16, 1 MI355X) at N=8K d=128 causal; % of MFMA peak "
                   "(useful FLOPs = 2.5x forward)")
+    if stdp:
+        metric = ("standard (materializing) attention fwd TFLOP/s (bf16, 1 MI355X) at N=8K "
+                  "d=128 causal; useful FLOPs as the flash forward")
     result = {
         "metric": metric,
         "value": round(value, 2),
@@ -325,6 +378,20 @@ def main(argv=None):
         },
         "cpu_baseline": None,
     }
+    if stdp:
+        result["roofline"] = {
+            "bound": "hbm",
+            "achieved": round(sm_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(sm_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(sm_ms, 5),
+            "kernels": list(PASS_KERNELS["std"]),
+            "algorithmic_bytes": sm_bytes,
+            "kernel_source_digest": digest,
+            "call_ms": round(avg_launch_ms, 5),
+        }
     if args.cpu_budget > 0:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do_cpu, args.cpu_budget) if bwd

@@ -48,7 +48,9 @@ typedef enum fa_status {
     FA_ERR_MISALIGNED = 5,          /* q/k/v/o not 16-byte aligned, lse not 4-byte */
     FA_ERR_ALIASING = 6,            /* an output overlaps an input or an output    */
     FA_ERR_LAUNCH = 7,              /* the HIP runtime rejected the launch         */
-    FA_ERR_TOO_LARGE = 8            /* B*H*ceil(N/128) workgroups exceed 2^31 - 1  */
+    FA_ERR_TOO_LARGE = 8,           /* B*H*ceil(N/128) workgroups exceed 2^31 - 1  */
+    FA_ERR_WORKSPACE = 9,           /* workspace NULL, misaligned or too small     */
+    FA_ERR_LIBRARY = 10             /* a library call (rocBLAS) failed             */
 } fa_status;
 
 /*

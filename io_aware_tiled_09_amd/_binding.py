@@ -19,7 +19,7 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEAD_DIM",
     4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_MISALIGNED", 6: "FA_ERR_ALIASING", 7: "FA_ERR_LAUNCH",
-    8: "FA_ERR_TOO_LARGE",
+    8: "FA_ERR_TOO_LARGE", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_LIBRARY",
 }
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string", "fa_tile_rows",
            "fa_tile_cols")

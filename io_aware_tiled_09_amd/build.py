@@ -1,4 +1,6 @@
-"""Compile the gfx950 HIP library ``libfa.so`` in-tree with hipcc."""
+"""Compile the gfx950 HIP libraries in-tree with hipcc: ``libfa.so`` (the
+FlashAttention forward and backward) and ``libfa_std.so`` (the standard,
+materializing attention baseline, which links rocBLAS)."""
 from __future__ import annotations
 
 import os
@@ -8,6 +10,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfa.so")
+STD_LIB = os.path.join(PKG, "libfa_std.so")
+STD_SOURCES = [os.path.join(PKG, "csrc", "fa_std.hip")]
 SOURCES = [os.path.join(PKG, "csrc", "fa_fwd_bf16.hip"),
            os.path.join(PKG, "csrc", "fa_bwd_bf16.hip"),
            os.path.join(PKG, "csrc", "fa_fwd_f32.hip"),
@@ -22,17 +26,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str = LIB) -> list:
+def command(out: str = LIB, sources=None, libs=()) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # no packed-fp32 VALU forms anywhere in the device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), "-o", out, *SOURCES]
+            "-I", os.path.join(ROOT, "include"), "-o", out, *(sources or SOURCES), *libs]
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles; writes libfa.so atomically next to this file."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def _compile(out, sources, libs=(), verbose=False):
+    tmp = out + ".tmp"
+    cmd = command(tmp, sources, libs)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,7 +45,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, flush=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles both libraries; writes them atomically next to this file."""
+    _compile(LIB, SOURCES, verbose=verbose)
+    _compile(STD_LIB, STD_SOURCES, ("-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"),
+             verbose=verbose)
     return LIB
 
 

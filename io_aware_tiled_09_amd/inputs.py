@@ -33,8 +33,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_dout", "sample_rows", "useful_flops",
-           "backward_flops"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_dout", "make_scores", "sample_rows",
+           "useful_flops", "backward_flops"]
 
 
 @dataclass(frozen=True)
@@ -151,6 +151,14 @@ def make_dout(w: Workload | str | None = None, *, B=None, H=None, N=None, d=None
     g = torch.Generator(device="cpu").manual_seed(int(seed or 0) + 500009)
     x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
     return _cast(x, dtype or "bf16")
+
+
+def make_scores(B: int, H: int, N: int, seed: int, std: float = 3.0) -> torch.Tensor:
+    """Score matrices for testing a row softmax on its own: contiguous fp32
+    [B, H, N, N], i.i.d. N(0, std^2) from torch.Generator('cpu') seeded with
+    ``seed``."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    return torch.randn((B, H, N, N), generator=g, dtype=torch.float32) * std
 
 
 def sample_rows(N: int, count: int, seed: int, heads: int = 1) -> torch.Tensor:

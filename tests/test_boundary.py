@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert fa.fa_status_string(0) == "ok"
-    for code in range(1, 9):
+    for code in range(1, 11):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -103,3 +103,58 @@ def test_bwd_argument_errors():
     assert _bwd(B=65536, H=65536, N=128) == 8
     for B, H, N in ((0, 4, 100), (2, 0, 100), (2, 4, 0)):
         assert fa.fa_bwd(*([None] * 10), B, H, N, 64, 0.125, 1, None) == 0
+
+
+# ---------------------------------------------------------------- libfa_std.so
+from io_aware_tiled_09_amd import standard as std  # noqa: E402
+
+STD_HEADER = os.path.join(ROOT, "include", "fa_std.h")
+
+
+def test_std_library_exports_every_declared_symbol():
+    lib = std.load_std()
+    text = re.sub(r"/\*.*?\*/", "", open(STD_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(fa_std_[a-z0-9_]+)\s*\(", text)))
+    assert set(names) == set(std.STD_EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_std_workspace_bytes():
+    nn = 2 * 3 * 100 * 100
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert std.fa_std_workspace_bytes(2, 3, 100) == r(nn * 4) + r(nn * 2) + (32 << 20)
+    assert std.fa_std_workspace_bytes(0, 3, 100) == 0
+    assert std.fa_std_workspace_bytes(-1, 3, 100) == 0
+    assert std.fa_std_workspace_bytes(2, 32, 8192) == 2 * 32 * 8192 * 8192 * 6 + (32 << 20)
+
+
+def _std(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+         ws=A + 512 * MB, ws_bytes=None, B=1, H=2, N=100, d=64, scale=0.125, causal=0):
+    if ws_bytes is None:
+        ws_bytes = std.fa_std_workspace_bytes(B, H, N)
+    return std.fa_std_fwd(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, scale, causal, 0)
+
+
+def test_std_argument_errors():
+    assert _std(q=0) == 1
+    assert _std(N=-1) == 2
+    assert _std(d=96) == 3
+    assert _std(scale=float("nan")) == 4
+    assert _std(o=A + 192 * MB + 8) == 5
+    assert _std(ws=0) == 9
+    assert _std(ws=A + 512 * MB + 16) == 9                 # not 256-byte aligned
+    assert _std(ws_bytes=1000) == 9                        # too small
+    assert _std(o=A) == 6                                  # o is q
+    assert _std(ws=A + 64 * MB) == 6                       # workspace over k
+    assert _std(B=65536, H=65536, N=2) == 8
+    for B, H, N in ((0, 4, 100), (2, 0, 100), (2, 4, 0)):
+        assert std.fa_std_fwd(*([None] * 6), 0, B, H, N, 64, 0.125, 1, None) == 0
+    # the three steps check their own arguments
+    assert std.fa_std_scores(A, A + 64 * MB, 0, A + 512 * MB, 1, 2, 100, 64, 0.1) == 1
+    assert std.fa_std_scores(A, A + 64 * MB, A + 128 * MB, 0, 1, 2, 100, 64, 0.1) == 9
+    assert std.fa_std_scores(A, A + 64 * MB, A, A + 512 * MB, 1, 2, 100, 64, 0.1) == 6
+    assert std.fa_std_softmax(A, A, A + 256 * MB, 1, 2, 100, 1) == 6
+    assert std.fa_std_softmax(A, A + 64 * MB + 2, A + 256 * MB, 1, 2, 100, 1) == 5
+    assert std.fa_std_output(A, A + 64 * MB, A + 64 * MB, A + 512 * MB, 1, 2, 100, 64) == 6
+    assert std.fa_std_output(A, A + 64 * MB, A + 128 * MB, A + 512 * MB, 1, 2, 100, 32) == 3

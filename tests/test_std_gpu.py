@@ -1,0 +1,115 @@
+"""GPU parity of the standard (materializing) attention baseline, libfa_std.so
+through its C ABI, against the fp64 oracle. The softmax step is also checked
+on its own against the oracle's direct softmax of each row.
+
+Bound on O, per element, from this path's rounding points: the scores and
+the exponentials are fp32 (relative error ~1e-7), the normalized P is
+rounded to bf16 (relative error <= 2^-8) before the fp32-accumulated product
+with V, and O is rounded to bf16 (<= 2^-8 |O|). So, to first order,
+    |O_gpu - O| <= 2^-8 (sum_j P_ij |V_jt| + |O_it|),
+and the test allows 1.05 times that plus 1e-5, with sum_j P_ij |V_jt| from
+the oracle run on |V|. (The flash path's dominant weight is an unnormalized
+exp2(0) = 1, exact in bf16, which is why the benchmark spec's bound of 2e-2 holds
+there even on spiky rows while it need not here.) Mean |dO| <= 2e-3 and lse
+as the flash path (tests/_parity.py)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_tiled_09_amd import standard as std
+from io_aware_tiled_09_amd.inputs import WORKLOADS, make_qkv, make_scores, sample_rows
+
+from _parity import LSE_REL, O_MEAN_ABS, say
+
+
+def assert_close_std(o, lse, o_ref, lse_ref, a_ref, label=""):
+    """o, lse: GPU results; o_ref, lse_ref: oracle; a_ref: oracle output on |V|."""
+    o = np.asarray(o, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    d = np.abs(o - o_ref)
+    bound = 1.05 * 2.0 ** -8 * (a_ref + np.abs(o_ref)) + 1e-5
+    ratio = d / bound
+    lrel = float((np.abs(lse - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)).max())
+    say(f"  {label}: max|dO|={d.max():.3e} mean|dO|={d.mean():.3e} max |dO|/bound="
+        f"{ratio.max():.3f} lse rel={lrel:.3e}")
+    assert ratio.max() <= 1.0, np.unravel_index(int(ratio.argmax()), d.shape)
+    assert d.mean() <= O_MEAN_ABS
+    assert lrel <= LSE_REL
+
+pytestmark = pytest.mark.gpu
+
+
+def run_std(q, k, v, causal, scale):
+    dq, dk, dv = (t.to("cuda:0") for t in (q, k, v))
+    o, lse = std.standard_attention(dq, dk, dv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.double().cpu(), lse.double().cpu()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 2, 17, 64, 127, 128, 257, 333, 512])
+def test_std_shapes(N, d, causal):
+    say(f"std N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B=2, H=2, N=N, d=d, seed=N * 3 + d)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, causal)
+    a_ref, _ = oracle.attention_fwd(q, k, v.abs(), scale, causal)
+    o, lse = run_std(q, k, v, causal, scale)
+    assert_close_std(o.numpy(), lse.numpy(), o_ref, lse_ref, a_ref, f"N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("name", ["bert512", "gpt2_1k", "gpt2_1k_spiky"])
+def test_std_workloads(name):
+    w = WORKLOADS[name]
+    say(f"std workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
+    q, k, v = make_qkv(w)
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, w.scale, w.causal)
+    a_ref, _ = oracle.attention_fwd(q, k, v.abs(), w.scale, w.causal)
+    o, lse = run_std(q, k, v, w.causal, w.scale)
+    assert_close_std(o.numpy(), lse.numpy(), o_ref, lse_ref, a_ref, name)
+
+
+def test_std_longdoc8k_sampled_rows():
+    w = WORKLOADS["longdoc8k"]
+    rows = torch.cat([sample_rows(w.N, 24, seed=w.seed + 55, heads=w.B * w.H),
+                      torch.tensor([0, 1, 4095, w.N - 2, w.N - 1]).expand(w.B * w.H, -1)], 1)
+    say(f"std workload longdoc8k, {rows.shape[1]} rows per head")
+    q, k, v = make_qkv(w)
+    o, lse = run_std(q, k, v, w.causal, w.scale)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, w.scale, w.causal, rows)
+    a_ref, _ = oracle.attention_rows(q, k, v.abs(), w.scale, w.causal, rows)
+    og = torch.gather(o.reshape(w.B * w.H, w.N, w.d), 1, rows.unsqueeze(-1).expand(-1, -1, w.d))
+    lg = torch.gather(lse.reshape(w.B * w.H, w.N), 1, rows)
+    assert_close_std(og.numpy(), lg.numpy(), o_ref, lse_ref, a_ref, "longdoc8k")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [5, 300, 1024])
+def test_std_softmax_step(N, causal):
+    """P and lse from given fp32 scores against the oracle's direct softmax of
+    each row (with V = identity, its output row is the probability row).
+    Bound: P is stored in bf16 (relative 2^-9) after an fp32 exp2; lse in fp32."""
+    say(f"std softmax step N={N} causal={causal}")
+    s = make_scores(1, 2, N, seed=N + 7)
+    gs = s.cuda()
+    p = torch.empty((1, 2, N, N), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((1, 2, N), dtype=torch.float32, device="cuda:0")
+    assert std.fa_std_softmax(gs, p, lse, 1, 2, N, causal) == 0
+    torch.cuda.synchronize()
+    p = p.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    eye = np.eye(N)
+    rows = range(N) if N <= 300 else [0, 1, 2, 511, 512, 1022, 1023]
+    for h in range(2):
+        for i in rows:
+            n = i + 1 if causal else N
+            p_ref, lse_ref = oracle.softmax_row(s[0, h, i, :n].double().numpy(), eye[:n, :n])
+            assert np.all(p[0, h, i, n:] == 0)
+            err = np.abs(p[0, h, i, :n] - p_ref)
+            assert np.all(err <= 2.0 ** -8 * p_ref + 1e-7), (h, i, err.max())
+            assert abs(lse[0, h, i] - lse_ref) <= 1e-5 * max(1.0, abs(lse_ref)), (h, i)
