@@ -51,7 +51,7 @@ PASS_SOURCES = {"fwd": ("fa_common.h", "fa_lds.h", "fa_fwd_bf16.hip"),
 # Kernel names (substrings) rocprofv3 reports for each pass.
 PASS_KERNELS = {"fwd": ("fa_fwd_bf16_kernel",),
                 "bwd": ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"),
-                "std": ("fa_std_softmax_kernel",)}
+                "std": ("fa_std_softmax",)}
 
 
 def log(*a):

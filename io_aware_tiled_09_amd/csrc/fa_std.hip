@@ -8,11 +8,11 @@
 //
 // Steps 1 and 3 are plain batched GEMMs and go to rocBLAS (bf16 inputs, fp32
 // accumulation). Step 2, the row softmax over the stored scores, is this
-// file's kernel: one workgroup of 256 threads per query row, fp32 scores
-// streamed with 16-byte loads, an online (max, sum) per thread merged across
-// the workgroup, then a second pass over the row (now in L2) that writes bf16
-// probabilities. It is HBM-bound: 4 bytes read per visible score and 2 bytes
-// written per entry of P.
+// file's kernel: one workgroup of 256 threads per query row. Rows of up to
+// 8192 scores (N % 4 == 0) are read once into registers with 16-byte loads;
+// longer or odd rows use an online (max, sum) per thread merged across the
+// workgroup and a second pass over the row (then in L2). Either way it is
+// HBM-bound: 4 bytes read per visible score and 2 bytes written per entry of P.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 #include <math.h>
@@ -124,6 +124,74 @@ __global__ __launch_bounds__(kSmThreads) void fa_std_softmax_kernel(const float*
     if (tid == 0) lse[row] = m + __builtin_amdgcn_logf(l) * kLn2F;
 }
 
+// Rows of up to kSmThreads * 4 * NV scores (N % 4 == 0): the visible part of
+// the row is read once into registers (NV 16-byte loads per thread, all in
+// flight together), then max, sum and the bf16 row of P come from there.
+template <bool CAUSAL, int NV>
+__global__ __launch_bounds__(kSmThreads) void fa_std_softmax_reg_kernel(const float* __restrict__ s,
+                                                                        __bf16* __restrict__ p,
+                                                                        float* __restrict__ lse,
+                                                                        int N)
+{
+    __shared__ float red[kSmThreads / 64];
+    const long long row = blockIdx.x;
+    const int i = (int)(row % N);
+    const int nvis = CAUSAL ? i + 1 : N;
+    const float* srow = s + row * (long long)N;
+    __bf16* prow = p + row * (long long)N;
+    const int tid = threadIdx.x;
+    const int n4 = N / 4;
+
+    f32x4 r[NV];
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+        const int j = 4 * (tid + c * kSmThreads);
+        r[c] = j < nvis ? *reinterpret_cast<const f32x4*>(srow + j)
+                        : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (j < nvis && j + 4 > nvis)  // the row's last visible float4
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e >= nvis) r[c][e] = -INFINITY;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+        m = fmaxf(m, fmaxf(fmaxf(r[c][0], r[c][1]), fmaxf(r[c][2], r[c][3])));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();  // red is reused for the sums
+    const float mc = m * kLog2eF;  // every row sees key 0: m is finite
+    float l = 0.f;
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[c][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(r[c][e], kLog2eF, -mc));  // -inf -> 0
+            l += r[c][e];
+        }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = l;
+    __syncthreads();
+    l = (red[0] + red[1]) + (red[2] + red[3]);
+    const float inv_l = 1.0f / l;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+        const int x = tid + c * kSmThreads;
+        if (x < n4) {
+            bf16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(r[c][e] * inv_l);
+            *reinterpret_cast<bf16x4*>(prow + 4 * x) = out;
+        }
+    }
+    if (tid == 0) lse[row] = m + __builtin_amdgcn_logf(l) * kLn2F;
+}
+static_assert(kSmThreads == 256, "the reductions above assume four waves");
+
 struct Range {
     uintptr_t lo, hi;
 };
@@ -213,7 +281,21 @@ int launch_softmax(const float* s, void* p, float* lse, int BH, int N, bool caus
     const dim3 grid((unsigned)((long long)BH * N));
     const bool vec = N % 4 == 0;
     __bf16* pb = static_cast<__bf16*>(p);
-    if (causal && vec)
+    if (vec && N <= kSmThreads * 4 * 8) {
+        const int nv = (N + kSmThreads * 4 - 1) / (kSmThreads * 4);  // 1..8
+#define FA_STD_REG(NV)                                                                          \
+    if (causal)                                                                                \
+        hipLaunchKernelGGL((fa_std_softmax_reg_kernel<true, NV>), grid, dim3(kSmThreads), 0,  \
+                           stream, s, pb, lse, N);                                             \
+    else                                                                                       \
+        hipLaunchKernelGGL((fa_std_softmax_reg_kernel<false, NV>), grid, dim3(kSmThreads), 0, \
+                           stream, s, pb, lse, N);
+        if (nv == 1) { FA_STD_REG(1) }
+        else if (nv == 2) { FA_STD_REG(2) }
+        else if (nv <= 4) { FA_STD_REG(4) }
+        else { FA_STD_REG(8) }
+#undef FA_STD_REG
+    } else if (causal && vec)
         hipLaunchKernelGGL((fa_std_softmax_kernel<true, true>), grid, dim3(kSmThreads), 0, stream, s, pb, lse, N);
     else if (causal)
         hipLaunchKernelGGL((fa_std_softmax_kernel<true, false>), grid, dim3(kSmThreads), 0, stream, s, pb, lse, N);
