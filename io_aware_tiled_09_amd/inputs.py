@@ -33,8 +33,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_dout", "make_scores", "sample_rows",
-           "useful_flops", "backward_flops"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_qkv_fp8", "make_dout", "make_scores",
+           "sample_rows", "useful_flops", "backward_flops"]
 
 
 @dataclass(frozen=True)
@@ -133,6 +133,25 @@ def make_qkv(w: Workload | str | None = None, *, B=None, H=None, N=None, d=None,
         k.mul_(c)
         v.mul_(c)
     return _cast(q, w.dtype), _cast(k, w.dtype), _cast(v, w.dtype)
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor FP8 E4M3 quantization of an fp32 tensor: scale = amax / 448
+    (448 is the format's largest finite value), codes = round-to-nearest-even
+    of x / scale (torch's float8_e4m3fn cast). Returns (uint8 codes, scale)."""
+    amax = float(x.abs().max())
+    scale = amax / 448.0 if amax > 0 else 1.0
+    codes = (x / scale).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return codes, scale
+
+
+def make_qkv_fp8(w: Workload | str | None = None, **kw):
+    """The workload's fp32 draws (as ``make_qkv`` with dtype "fp32"), each
+    quantized per tensor to FP8 E4M3. Returns ((q8, k8, v8) uint8 CPU tensors,
+    (q_scale, k_scale, v_scale) floats)."""
+    q, k, v = make_qkv(w, dtype="fp32", **kw)
+    (q8, qs), (k8, ks), (v8, vs) = (quantize_e4m3(t) for t in (q, k, v))
+    return (q8, k8, v8), (qs, ks, vs)
 
 
 def make_dout(w: Workload | str | None = None, *, B=None, H=None, N=None, d=None,

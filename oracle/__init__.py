@@ -21,6 +21,11 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
 * ``attention_bwd_sampled``: the full ``attention_bwd`` on small inputs and
   torch's CPU float64 autograd (it evaluates D as dO . O instead of
   sum_j P_ij dP_ij, and P from lse instead of a stored row).
+* ``decode_e4m3``: torch's float8_e4m3fn -> float64 conversion of all 254
+  non-NaN codes, and the format's closed forms (1.0 = 0x38, 448 = 0x7E, the
+  smallest subnormal 2^-9 = 0x01, signs).
+* ``attention_fwd_fp8``: ``decode_e4m3`` followed by ``attention_fwd`` (no
+  arithmetic of its own).
 * ``attention_bwd``: central finite differences of the forward oracle's loss
   sum(dO * O) on tiny inputs, torch's CPU float64 autograd of
   scaled_dot_product_attention, the identities D = rowsum(dO * O) and
@@ -80,6 +85,8 @@ def _load():
         _dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
         ctypes.c_double, ctypes.c_int, _lp, ctypes.c_long, _lp, ctypes.c_long, _lp,
         ctypes.c_long, _dp, _dp, _dp]
+    lib.oracle_decode_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_double, _dp]
+    lib.oracle_decode_e4m3.restype = ctypes.c_int
     for name in ("oracle_softmax_row", "oracle_online_row_two_scale",
                  "oracle_online_row_single_max", "oracle_attention_fwd",
                  "oracle_attention_rows", "oracle_attention_bwd",
@@ -245,3 +252,32 @@ def attention_bwd_sampled(q, k, v, dout, scale, causal, heads, qrows, krows):
         hs.ctypes.data_as(_lp), hs.size, qr.ctypes.data_as(_lp), R, kr.ctypes.data_as(_lp), C,
         _ptr(dq), _ptr(dk), _ptr(dv)), "attention_bwd_sampled")
     return dq, dk, dv
+
+
+def decode_e4m3(x, scale=1.0) -> np.ndarray:
+    """Exact fp64 values of FP8 E4M3 codes (uint8 array or torch uint8 /
+    float8_e4m3fn tensor), times ``scale``; same shape."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().cpu()
+        if x.dtype != torch.uint8:
+            x = x.view(torch.uint8)
+        x = x.numpy()
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.uint8))
+    out = np.empty(a.shape, dtype=np.float64)
+    _check(_load().oracle_decode_e4m3(a.ctypes.data_as(ctypes.c_void_p), a.size, float(scale),
+                                      _ptr(out)), "decode_e4m3")
+    return out
+
+
+def attention_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal):
+    """Standard attention on the decoded 8-bit inputs: Q = q_scale * decode(q8),
+    likewise K and V, then ``attention_fwd``. Returns (o, lse)."""
+    return attention_fwd(decode_e4m3(q8, q_scale), decode_e4m3(k8, k_scale),
+                         decode_e4m3(v8, v_scale), scale, causal)
+
+
+def attention_rows_fp8(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal, rows):
+    """``attention_rows`` on the decoded 8-bit inputs."""
+    return attention_rows(decode_e4m3(q8, q_scale), decode_e4m3(k8, k_scale),
+                          decode_e4m3(v8, v_scale), scale, causal, rows)

@@ -583,3 +583,26 @@ int oracle_attention_bwd_sampled(const double *q, const double *k,
     free(scratch);
     return ORACLE_OK;
 }
+
+/*
+ * FP8 E4M3 (the OCP 8-bit floating-point format with 4 exponent bits, bias
+ * 7, 3 mantissa bits, no infinities; S.1111.111 is NaN) decoded to fp64:
+ * exponent field 0 is subnormal, value (m / 8) * 2^-6; otherwise
+ * (1 + m / 8) * 2^(e - 7). Used to hand the exact values of 8-bit inputs,
+ * times their per-tensor scale, to the attention definitions above.
+ * x: n bytes; out: n doubles (each times `scale`). Returns ORACLE_ERR_ARG on
+ * a NaN code.
+ */
+int oracle_decode_e4m3(const unsigned char *x, long n, double scale, double *out)
+{
+    if (n < 0 || (n > 0 && (!x || !out)))
+        return ORACLE_ERR_ARG;
+    for (long t = 0; t < n; ++t) {
+        const int s = x[t] >> 7, e = (x[t] >> 3) & 15, m = x[t] & 7;
+        if (e == 15 && m == 7)
+            return ORACLE_ERR_ARG;
+        const double mag = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+        out[t] = (s ? -mag : mag) * scale;
+    }
+    return ORACLE_OK;
+}

@@ -396,3 +396,31 @@ def test_bwd_sampled_matches_torch_autograd_and_full(causal):
         oracle.attention_bwd_sampled(q, k, v, do, scale, causal, [6], [0], [0])
     with pytest.raises(ValueError):
         oracle.attention_bwd_sampled(q, k, v, do, scale, causal, [0], [37], [0])
+
+
+# ---------------------------------------------------------------- FP8 E4M3 decoding
+def test_decode_e4m3_matches_torch_for_every_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.decode_e4m3(codes), ref)
+    np.testing.assert_array_equal(oracle.decode_e4m3(codes, 0.5), ref * 0.5)
+
+
+def test_decode_e4m3_closed_forms():
+    got = oracle.decode_e4m3(np.array([0x38, 0x7E, 0x01, 0x08, 0x00, 0x80, 0xB8, 0x39, 0x07],
+                                      dtype=np.uint8))
+    assert list(got) == [1.0, 448.0, 2.0 ** -9, 2.0 ** -6, 0.0, -0.0, -1.0, 1.125,
+                         7 * 2.0 ** -9]
+    with pytest.raises(ValueError):
+        oracle.decode_e4m3(np.array([0x7F], dtype=np.uint8))
+
+
+def test_attention_fwd_fp8_is_attention_of_decoded_inputs():
+    rng = np.random.default_rng(11)
+    codes = [rng.integers(0, 0x7E, size=(1, 2, 9, 4)).astype(np.uint8) |
+             (rng.integers(0, 2, size=(1, 2, 9, 4)).astype(np.uint8) << 7) for _ in range(3)]
+    o, lse = oracle.attention_fwd_fp8(*codes, 0.01, 0.02, 0.5, 0.7, True)
+    deq = [torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64) * s
+           for c, s in zip(codes, (0.01, 0.02, 0.5))]
+    ref = torch.nn.functional.scaled_dot_product_attention(*deq, is_causal=True, scale=0.7)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12, rtol=1e-10)
