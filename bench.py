@@ -19,6 +19,10 @@ O = PV by rocBLAS) on the same workload; `value` counts the same useful
 FLOPs as the flash forward, and the roofline object is the softmax kernel's
 (HBM-bound: visible fp32 scores read, bf16 P written).
 
+With --pass fp8 one step is one FP8 forward call (fa_fwd_fp8) on the same
+workload's draws quantized per tensor to E4M3; `value` counts the same useful
+FLOPs and the roofline peak is the FP8 MFMA rate (5.0 PFLOP/s dense).
+
 With --pass bwd one step is one backward call (fa_bwd: the D, dK/dV and dQ
 kernels) on the same workload with a seeded N(0,1) dO, O and lse from one
 forward call made before timing; `value` is useful backward TFLOP/s
@@ -39,19 +43,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k.json"),
                  "bwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_bwd.json"),
-                 "std": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_std.json")}
+                 "std": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_std.json"),
+                 "fp8": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_fp8.json")}
 # Sources each pass's kernels are compiled from (the traffic summary is valid
 # only for the exact sources it was taken on).
 PASS_SOURCES = {"fwd": ("fa_common.h", "fa_lds.h", "fa_fwd_bf16.hip"),
                 "bwd": ("fa_common.h", "fa_lds.h", "fa_bwd_bf16.hip"),
-                "std": ("fa_common.h", "fa_std.hip")}
+                "std": ("fa_common.h", "fa_std.hip"),
+                "fp8": ("fa_common.h", "fa_lds.h", "fa_fwd_fp8.hip")}
 # Kernel names (substrings) rocprofv3 reports for each pass.
 PASS_KERNELS = {"fwd": ("fa_fwd_bf16_kernel",),
                 "bwd": ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"),
-                "std": ("fa_std_softmax",)}
+                "std": ("fa_std_softmax",),
+                "fp8": ("fa_fwd_fp8_kernel",)}
 
 
 def log(*a):
@@ -137,8 +145,10 @@ def ingest_counters(fetch_csv, write_csv, copy_mib, command, pass_="fwd"):
     return 0
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
-    """Time the oracle over whole heads of the workload until about budget_s."""
+def cpu_baseline(w, q, k, v, budget_s: float, fp8=None):
+    """Time the oracle over whole heads of the workload until about budget_s.
+    fp8: ((q8, k8, v8), (q_scale, k_scale, v_scale)) to time the oracle on the
+    decoded 8-bit inputs instead."""
     import oracle
     B, H, N, d = q.shape
     heads, elapsed = 0, 0.0
@@ -147,7 +157,11 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         b, h = divmod(heads, H)
         sl = (slice(b, b + 1), slice(h, h + 1))
         t0 = time.perf_counter()
-        oracle.attention_fwd(q[sl], k[sl], v[sl], w.scale, w.causal)
+        if fp8 is None:
+            oracle.attention_fwd(q[sl], k[sl], v[sl], w.scale, w.causal)
+        else:
+            (q8, k8, v8), sc = fp8
+            oracle.attention_fwd_fp8(q8[sl], k8[sl], v8[sl], *sc, w.scale, w.causal)
         elapsed += time.perf_counter() - t0
         heads += 1
         log(f"  oracle head {heads}: {elapsed:.1f} s")
@@ -158,7 +172,8 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"{heads} of {B * H} heads (all {N} query rows each) of {w.name}, "
+        "sample": f"{heads} of {B * H} heads (all {N} query rows each) of {w.name}"
+                  f"{' (decoded FP8 inputs)' if fp8 is not None else ''}, "
                   f"fp64 with S and P materialized; useful FLOPs of the sample / "
                   f"{elapsed:.1f} s wall (incl. the fp64 upcast: {time.perf_counter() - t_start:.1f} s)",
     }
@@ -196,10 +211,11 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="longdoc8k")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "std"), default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "std", "fp8"), default="fwd",
                     help="fwd: one step = one forward call (the default line); bwd: one "
                          "step = one backward call (fa_bwd) given O and lse; std: one step = "
-                         "the standard materializing forward (S and P through HBM)")
+                         "the standard materializing forward (S and P through HBM); fp8: one "
+                         "step = one FP8 (E4M3) forward call (fa_fwd_fp8)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
@@ -249,9 +265,24 @@ def main(argv=None):
         if st != 0:
             raise fa.FAError(st)
 
+    fp8 = args.pass_ == "fp8"
     stdp = args.pass_ == "std"
     std_sm = None  # (start, end) event pairs around the softmax launches
-    if stdp:
+    if fp8:
+        from io_aware_tiled_09_amd.inputs import make_qkv_fp8
+        if w.d != 128:
+            print("the FP8 forward takes d = 128 only", file=sys.stderr)
+            return 2
+        (q8, k8, v8), (qs, ks, vs) = make_qkv_fp8(w)
+        g8 = [t.to(dev) for t in (q8, k8, v8)]
+        del dq, dk, dv
+
+        def step():
+            st = fa.fa_fwd_fp8(*g8, o, lse, w.B, w.H, w.N, w.d, w.scale, qs, ks, vs, w.causal,
+                               stream)
+            if st != 0:
+                raise fa.FAError(st)
+    elif stdp:
         from io_aware_tiled_09_amd import standard as stdlib
         need = stdlib.fa_std_workspace_bytes(w.B, w.H, w.N)
         ws8 = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -345,6 +376,9 @@ def main(argv=None):
     if bwd:
         metric = ("attention bwd TFLOP/s (bf16, 1 MI355X) at N=8K d=128 causal; % of MFMA peak "
                   "(useful FLOPs = 2.5x forward)")
+    if fp8:
+        metric = ("attention fwd TFLOP/s with FP8 (E4M3) Q, K, V (1 MI355X) at N=8K d=128 causal; "
+                  "% of the FP8 MFMA peak")
     if stdp:
         metric = ("standard (materializing) attention fwd TFLOP/s (bf16, 1 MI355X) at N=8K "
                   "d=128 causal; useful FLOPs as the flash forward")
@@ -378,6 +412,12 @@ def main(argv=None):
         },
         "cpu_baseline": None,
     }
+    if fp8:
+        result["dtype"] = "fp8_e4m3"
+        result["pct_of_peak"] = round(100.0 * value / PEAK_FP8_TFLOPS, 2)
+        result["roofline"]["peak"] = PEAK_FP8_TFLOPS
+        result["roofline"]["frac"] = round(achieved / PEAK_FP8_TFLOPS, 4)
+        result["roofline"]["kernels"] = list(PASS_KERNELS["fp8"])
     if stdp:
         result["roofline"] = {
             "bound": "hbm",
@@ -395,7 +435,8 @@ def main(argv=None):
     if args.cpu_budget > 0:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do_cpu, args.cpu_budget) if bwd
-                                  else cpu_baseline(w, q, k, v, args.cpu_budget))
+                                  else cpu_baseline(w, q, k, v, args.cpu_budget,
+                                                    ((q8, k8, v8), (qs, ks, vs)) if fp8 else None))
     print(json.dumps(result), flush=True)
     return 0
 

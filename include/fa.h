@@ -102,6 +102,26 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            float *ws, int B, int H, int N, int d, float scale, int causal,
            void *stream);
 
+/*
+ * FP8 attention forward: Q, K and V as 8-bit E4M3 codes (OCP FP8 E4M3: 4
+ * exponent bits, bias 7, 3 mantissa bits, no infinities) with one positive
+ * scale per tensor, so that the attended values are q_scale * Q, k_scale * K
+ * and v_scale * V; everything else as fa_fwd.
+ * [FlashAttention: The GPU Memory Hack That Changed Everything
+ *  (ai.branddocks.com, episode 75), "FlashAttention-3: Hopper Architecture":
+ *  attention in FP8 on the matrix units]
+ * q, k, v: const uint8 [B][H][N][d] codes (16-byte aligned); o: bf16
+ * [B][H][N][d]; lse: fp32 [B][H][N], natural log of the scaled scores;
+ * d == 128 only (FA_ERR_UNSUPPORTED_HEAD_DIM otherwise); scale >= 0 and
+ * finite; q_scale, k_scale, v_scale > 0 and finite (FA_ERR_BAD_SCALE).
+ * Both products run on the FP8 matrix instructions with fp32 accumulation;
+ * the softmax weights are rounded to E4M3 (as 256 p) for the second product.
+ * Codes 0x7F and 0xFF (NaN) propagate as NaN.
+ */
+int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int H, int N, int d, float scale, float q_scale,
+               float k_scale, float v_scale, int causal, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_string(int status);
 

@@ -21,7 +21,7 @@ STATUS_NAMES = {
     4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_MISALIGNED", 6: "FA_ERR_ALIASING", 7: "FA_ERR_LAUNCH",
     8: "FA_ERR_TOO_LARGE", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_LIBRARY",
 }
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string", "fa_tile_rows",
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_status_string", "fa_tile_rows",
            "fa_tile_cols")
 
 
@@ -45,6 +45,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         fn.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, f, f, f, i, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -87,6 +89,16 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
     """C fa_fwd_f32: as fa_fwd with fp32 q, k, v and o."""
     return int(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
                                  int(H), int(N), int(d), float(scale), int(bool(causal)),
+                                 _stream(stream, (q, k, v, o, lse))))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, q_scale, k_scale, v_scale, causal,
+               stream=None) -> int:
+    """C fa_fwd_fp8: uint8 E4M3 codes q, k, v [B,H,N,d] with per-tensor scales,
+    bf16 o, fp32 lse. Returns the fa_status code."""
+    return int(load().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                 int(N), int(d), float(scale), float(q_scale), float(k_scale),
+                                 float(v_scale), int(bool(causal)),
                                  _stream(stream, (q, k, v, o, lse))))
 
 
@@ -162,3 +174,27 @@ def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=N
     if st != FA_OK:
         raise FAError(st)
     return dq, dk, dv
+
+
+def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None, stream=None):
+    """Allocate o (bf16) and lse with torch and run the FP8 forward pass.
+
+    q8, k8, v8: contiguous uint8 [B, H, N, 128] CUDA tensors of E4M3 codes;
+    *_scale: the per-tensor scales. Returns (o, lse); raises FAError on a status.
+    """
+    import torch
+    ts = (q8, k8, v8)
+    if q8.dim() != 4 or any(t.shape != q8.shape for t in ts):
+        raise ValueError("q8, k8, v8 must share one [B, H, N, d] shape")
+    if any(t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() for t in ts):
+        raise ValueError("q8, k8, v8 must be contiguous uint8 GPU tensors")
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    st = fa_fwd_fp8(q8, k8, v8, o, lse, B, H, N, d, scale, q_scale, k_scale, v_scale, causal,
+                    stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse

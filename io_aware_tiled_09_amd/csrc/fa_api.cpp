@@ -95,6 +95,45 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, float q_scale, float k_scale, float v_scale, int causal,
+               void* stream)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return FA_ERR_BAD_SHAPE;
+    if (B == 0 || H == 0 || N == 0)
+        return FA_OK;
+    if (!q || !k || !v || !o || !lse)
+        return FA_ERR_NULL_PTR;
+    if (d != 128)
+        return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!isfinite(scale) || scale < 0.0f)
+        return FA_ERR_BAD_SCALE;
+    for (float t : {q_scale, k_scale, v_scale})
+        if (!isfinite(t) || t <= 0.0f)
+            return FA_ERR_BAD_SCALE;
+    const long long nqb = ((long long)N + fa::kBr - 1) / fa::kBr;
+    if ((long long)B * H * nqb > 0x7fffffffLL)
+        return FA_ERR_TOO_LARGE;
+    auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
+    if ((addr(q) | addr(k) | addr(v) | addr(o)) & 15u || (addr(lse) & 3u))
+        return FA_ERR_MISALIGNED;
+    const uintptr_t in_bytes = (uintptr_t)B * (uintptr_t)H * (uintptr_t)N * (uintptr_t)d;
+    const uintptr_t rows = (uintptr_t)B * (uintptr_t)H * (uintptr_t)N;
+    const Range rq{addr(q), addr(q) + in_bytes}, rk{addr(k), addr(k) + in_bytes},
+        rv{addr(v), addr(v) + in_bytes}, ro{addr(o), addr(o) + 2 * in_bytes},
+        rl{addr(lse), addr(lse) + rows * sizeof(float)};
+    if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv) || overlaps(ro, rl) ||
+        overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv))
+        return FA_ERR_ALIASING;
+    // The scores' constant folds the two input scales in; kept > 0 as in fa_fwd.
+    const double c = (double)scale * (double)q_scale * (double)k_scale * kLog2e;
+    const float c_log2 = c < FLT_MIN ? FLT_MIN : (float)c;
+    const hipError_t e = fa::launch_fp8(q, k, v, o, lse, B * H, N, c_log2, v_scale, causal != 0,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N, int d,
            float scale, int causal, void* stream)

@@ -23,4 +23,9 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            float* delta, int BH, int N, int d, float scale_log2, float scale,
                            bool causal, hipStream_t stream);
 
+// FP8 E4M3 forward (d = 128): q, k, v hold E4M3 codes; c_log2 = scale *
+// q_scale * k_scale * log2(e) > 0; out_scale = v_scale.
+hipError_t launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                      int N, float c_log2, float out_scale, bool causal, hipStream_t stream);
+
 }  // namespace fa

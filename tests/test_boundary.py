@@ -82,6 +82,27 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         _binding.fa_fwd(A, A, A, A, A, 1, 1, 1, 64, 1.0, 0)
 
 
+def _fp8(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, B=1, H=2, N=100,
+         d=128, scale=0.1, qs=0.01, ks=0.01, vs=0.01, causal=1):
+    return fa.fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, qs, ks, vs, causal, 0)
+
+
+def test_fp8_argument_errors():
+    assert _fp8(v=0) == 1
+    assert _fp8(H=-2) == 2
+    assert _fp8(d=64) == 3
+    assert _fp8(scale=float("inf")) == 4
+    assert _fp8(qs=0.0) == 4
+    assert _fp8(vs=float("nan")) == 4
+    assert _fp8(ks=-1.0) == 4
+    assert _fp8(k=A + 64 * MB + 4) == 5
+    assert _fp8(o=A + 64 * MB) == 6                 # o over k
+    assert _fp8(lse=A + 192 * MB + 1024) == 6       # lse inside o
+    assert _fp8(B=65536, H=65536, N=128) == 8
+    for B, H, N in ((0, 4, 100), (2, 0, 100), (2, 4, 0)):
+        assert fa.fa_fwd_fp8(None, None, None, None, None, B, H, N, 128, 0.1, 1, 1, 1, 1, None) == 0
+
+
 def _bwd(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
          dout=A + 320 * MB, dq=A + 384 * MB, dk=A + 448 * MB, dv=A + 512 * MB, ws=A + 576 * MB,
          B=1, H=2, N=100, d=64, scale=0.125, causal=0):

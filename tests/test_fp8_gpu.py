@@ -1,0 +1,100 @@
+"""GPU parity of the FP8 (E4M3) forward, fa_fwd_fp8 through the C ABI, against
+the fp64 oracle run on the decoded 8-bit inputs (oracle.attention_fwd_fp8).
+
+Bound on O, per element, from the kernel's rounding points: the scores are
+exact products of 8-bit values summed in fp32, the softmax is fp32; the
+weights are rounded to E4M3 (as 256 p: relative error <= 2^-4) before the
+product with V, and O is rounded to bf16 (<= 2^-8 |O|). To first order
+    |O_gpu - O| <= 2^-4 sum_j P_ij |V_jt| + 2^-8 |O_it|,
+with sum_j P_ij |V_jt| from the oracle run on |V|; the test allows that
+plus 1e-4 (weights below the E4M3 normal range, 256 p < 2^-6, round with an
+absolute error of at most 2^-18 in p). An fp32 emulation of exactly these
+rounding points on N from 17 to 2048 reaches at most 0.68 of the bound, and
+its mean |dO| at most 0.12 of the bound's mean; the test asks for mean
+|dO| <= 0.25 of it. lse is fp32 from exact scores: relative error <= 1e-3 as
+the bf16 path."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_09_amd as fa
+import oracle
+from io_aware_tiled_09_amd.inputs import WORKLOADS, make_qkv_fp8, sample_rows
+
+from _parity import LSE_REL, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fp8(codes, scales, causal, scale):
+    g = [c.to("cuda:0") for c in codes]
+    o, lse = fa.attention_fp8(*g, *scales, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def assert_close_fp8(o, lse, o_ref, lse_ref, a_ref, label=""):
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    d = np.abs(o - o_ref)
+    bound = 2.0 ** -4 * a_ref + 2.0 ** -8 * np.abs(o_ref) + 1e-4
+    lrel = float((np.abs(lse - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)).max())
+    say(f"  {label}: max|dO|={d.max():.3e} mean|dO|={d.mean():.3e} max |dO|/bound="
+        f"{(d / bound).max():.3f} mean ratio={d.mean() / bound.mean():.3f} lse rel={lrel:.3e}")
+    assert (d <= bound).all(), np.unravel_index(int((d / bound).argmax()), d.shape)
+    assert d.mean() <= 0.25 * bound.mean()
+    assert lrel <= LSE_REL
+
+
+def check_full(codes, scales, causal, scale, label):
+    o_ref, lse_ref = oracle.attention_fwd_fp8(*codes, *scales, scale, causal)
+    deq = [oracle.decode_e4m3(c, s) for c, s in zip(codes, scales)]
+    a_ref, _ = oracle.attention_fwd(deq[0], deq[1], np.abs(deq[2]), scale, causal)
+    o, lse = run_fp8(codes, scales, causal, scale)
+    assert_close_fp8(o, lse, o_ref, lse_ref, a_ref, label)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 257, 333])
+def test_fp8_shapes(N, causal):
+    say(f"fp8 N={N} causal={causal}")
+    codes, scales = make_qkv_fp8(B=1, H=2, N=N, d=128, seed=N * 5 + 1)
+    check_full(codes, scales, causal, 1.0 / math.sqrt(128), f"N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("name", ["gpt2_1k", "gpt2_1k_spiky"])
+def test_fp8_gpt2_shape_d128(name):
+    say(f"fp8 {name} with d=128, B=2 H=4")
+    codes, scales = make_qkv_fp8(name, B=2, H=4, d=128)
+    check_full(codes, scales, True, 1.0 / math.sqrt(128), name)
+
+
+def test_fp8_explicit_scale_and_scales():
+    say("fp8 scale=0.3, non-unit tensor scales, N=300")
+    codes, scales = make_qkv_fp8(B=1, H=3, N=300, d=128, seed=77)
+    check_full(codes, (scales[0] * 3.0, scales[1] * 0.5, scales[2] * 2.0), True, 0.3, "scale=0.3")
+
+
+def test_fp8_longdoc8k_sampled_rows():
+    w = WORKLOADS["longdoc8k"]
+    codes, scales = make_qkv_fp8(w)
+    rows = torch.cat([sample_rows(w.N, 24, seed=w.seed + 66, heads=w.B * w.H),
+                      torch.tensor([0, 63, 64, 127, 128, w.N - 2, w.N - 1]).expand(w.B * w.H, -1)], 1)
+    say(f"fp8 longdoc8k, {rows.shape[1]} rows per head")
+    o, lse = run_fp8(codes, scales, True, w.scale)
+    o_ref, lse_ref = oracle.attention_rows_fp8(*codes, *scales, w.scale, True, rows)
+    deq = [oracle.decode_e4m3(c, s) for c, s in zip(codes, scales)]
+    a_ref, _ = oracle.attention_rows(deq[0], deq[1], np.abs(deq[2]), w.scale, True, rows)
+    r = rows.numpy()
+    og = np.take_along_axis(o.reshape(w.B * w.H, w.N, w.d), r[:, :, None], axis=1)
+    lg = np.take_along_axis(lse.reshape(w.B * w.H, w.N), r, axis=1)
+    assert_close_fp8(og, lg, o_ref, lse_ref, a_ref, "longdoc8k")
+
+
+def test_fp8_deterministic_bitwise():
+    say("fp8 determinism B=2 H=2 N=1000 causal")
+    codes, scales = make_qkv_fp8(B=2, H=2, N=1000, d=128, seed=9)
+    a = run_fp8(codes, scales, True, 0.1)
+    b = run_fp8(codes, scales, True, 0.1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
