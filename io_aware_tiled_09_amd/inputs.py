@@ -34,7 +34,8 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_qkv", "make_qkv_fp8", "make_dout", "make_scores",
-           "sample_rows", "useful_flops", "backward_flops"]
+           "sample_rows", "useful_flops", "backward_flops", "DecodeWorkload", "DECODE_WORKLOADS",
+           "make_decode", "decode_kv_bytes"]
 
 
 @dataclass(frozen=True)
@@ -215,3 +216,105 @@ def backward_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     the forward's useful FLOPs."""
     f = 10.0 * B * H * N * N * d
     return f / 2.0 if causal else f
+
+
+
+# ---------------------------------------------------------------- decode over a paged KV cache
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step of B concurrent sequences: one new query token each,
+    attending to its L_b cached tokens stored in pages of ``page_size`` rows.
+
+    Lengths are drawn uniformly from [min_len, max_len_draw]; the page table
+    has room for ``max_context`` tokens per sequence. Physical pages are
+    handed out in a seeded random order (a fragmented pool), with
+    ``spare_pages`` extra pages that no sequence uses."""
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    d: int
+    page_size: int
+    max_context: int
+    min_len: int
+    max_len_draw: int
+    seed: int
+    spare_pages: int = 64
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def max_pages(self) -> int:
+        return (self.max_context + self.page_size - 1) // self.page_size
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        # 50 users served at once, memory sized for an 8K context, about 30%
+        # of it in use on average (mean length ~2460 of 8192).
+        # [FlashAttention: The GPU Memory Hack That Changed Everything,
+        #  "What's Next?": 50 concurrent users, pre-allocated max-context
+        #  memory mostly unused; PagedAttention's pages and page tables]
+        DecodeWorkload("decode50", 50, 32, 32, 128, 16, 8192, 64, 4864, 2001,
+                       note="50 sequences, MHA, 16-token pages"),
+        DecodeWorkload("decode50_gqa", 50, 32, 8, 128, 16, 8192, 64, 4864, 2002,
+                       note="the same with 4 query heads per KV head"),
+        DecodeWorkload("decode_small", 3, 4, 2, 128, 16, 1024, 1, 700, 2003,
+                       note="small case for the oracle in seconds"),
+    ]
+}
+
+
+def make_decode(w: DecodeWorkload | str, fill_unused=float("nan"), **over):
+    """Seeded inputs of one decode step. Returns a dict with q [B, H, d] bf16,
+    k_cache, v_cache [num_pages, H_kv, page_size, d] bf16, page_table int32
+    [B, max_pages] (-1 past each sequence's last page) and seq_lens int32 [B].
+
+    Draw order from torch.Generator('cpu').manual_seed(seed): the lengths,
+    the permutation of physical pages, then q, k_cache, v_cache as N(0, 1)
+    fp32 cast to bf16. Cache rows that no sequence owns (spare pages and the
+    rows after each sequence's last token) are set to ``fill_unused`` (NaN by
+    default, so that reading them would show)."""
+    if isinstance(w, str):
+        w = DECODE_WORKLOADS[w]
+    if over:
+        w = DecodeWorkload(**{**w.__dict__, **over})
+    g = torch.Generator(device="cpu").manual_seed(int(w.seed))
+    lens = torch.randint(w.min_len, w.max_len_draw + 1, (w.B,), generator=g, dtype=torch.int64)
+    lens = torch.clamp(lens, max=w.max_context)
+    pages_per = (lens + w.page_size - 1) // w.page_size
+    used = int(pages_per.sum())
+    num_pages = used + w.spare_pages
+    perm = torch.randperm(num_pages, generator=g)
+    table = torch.full((w.B, w.max_pages), -1, dtype=torch.int32)
+    at = 0
+    for b in range(w.B):
+        n = int(pages_per[b])
+        table[b, :n] = perm[at:at + n].to(torch.int32)
+        at += n
+    q = torch.randn((w.B, w.H, w.d), generator=g, dtype=torch.float32)
+    kc = torch.randn((num_pages, w.H_kv, w.page_size, w.d), generator=g, dtype=torch.float32)
+    vc = torch.randn((num_pages, w.H_kv, w.page_size, w.d), generator=g, dtype=torch.float32)
+    owned = torch.zeros((num_pages, w.page_size), dtype=torch.bool)
+    for b in range(w.B):
+        L = int(lens[b])
+        for t in range(int(pages_per[b])):
+            rows = min(w.page_size, L - t * w.page_size)
+            owned[int(table[b, t]), :rows] = True
+    mask = (~owned)[:, None, :, None].expand_as(kc)
+    kc[mask] = fill_unused
+    vc[mask] = fill_unused
+    return dict(q=q.to(torch.bfloat16), k_cache=kc.to(torch.bfloat16),
+                v_cache=vc.to(torch.bfloat16), page_table=table,
+                seq_lens=lens.to(torch.int32), workload=w)
+
+
+def decode_kv_bytes(w: DecodeWorkload, seq_lens) -> int:
+    """Algorithmic bytes of one decode step: every cached K and V row of every
+    sequence read once (bf16), q read and o written once (bf16), lse (fp32)."""
+    tokens = int(torch.as_tensor(seq_lens).sum())
+    return tokens * w.H_kv * w.d * 2 * 2 + w.B * w.H * (w.d * 2 * 2 + 4)

@@ -26,6 +26,11 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
   smallest subnormal 2^-9 = 0x01, signs).
 * ``attention_fwd_fp8``: ``decode_e4m3`` followed by ``attention_fwd`` (no
   arithmetic of its own).
+* ``decode_paged``: ``attention_rows`` on the same rows stored contiguously
+  (the last row of each sequence attending to all earlier ones), torch's
+  float64 SDPA on the gathered rows, invariance under a permutation of the
+  physical pages (with the table permuted alike), and query-head groups
+  sharing one KV head equal to repeating that head.
 * ``attention_bwd``: central finite differences of the forward oracle's loss
   sum(dO * O) on tiny inputs, torch's CPU float64 autograd of
   scaled_dot_product_attention, the identities D = rowsum(dO * O) and
@@ -85,6 +90,10 @@ def _load():
         _dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
         ctypes.c_double, ctypes.c_int, _lp, ctypes.c_long, _lp, ctypes.c_long, _lp,
         ctypes.c_long, _dp, _dp, _dp]
+    _ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_decode_paged.argtypes = [_dp, _dp, _dp, _ip, _ip] + [ctypes.c_long] * 7 + [
+        ctypes.c_double, _dp, _dp]
+    lib.oracle_decode_paged.restype = ctypes.c_int
     lib.oracle_decode_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_double, _dp]
     lib.oracle_decode_e4m3.restype = ctypes.c_int
     for name in ("oracle_softmax_row", "oracle_online_row_two_scale",
@@ -281,3 +290,29 @@ def attention_rows_fp8(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal, row
     """``attention_rows`` on the decoded 8-bit inputs."""
     return attention_rows(decode_e4m3(q8, q_scale), decode_e4m3(k8, k_scale),
                           decode_e4m3(v8, v_scale), scale, causal, rows)
+
+
+def decode_paged(q, k_cache, v_cache, page_table, seq_lens, scale):
+    """Decode-step attention over a paged KV cache.
+
+    q: [B, H, d]; k_cache, v_cache: [num_pages, H_kv, page_size, d];
+    page_table: int [B, max_pages]; seq_lens: int [B]. Query head h reads KV
+    head h // (H // H_kv). Returns (o [B, H, d], lse [B, H]).
+    """
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    pt = page_table.numpy() if hasattr(page_table, "numpy") else page_table
+    sl = seq_lens.numpy() if hasattr(seq_lens, "numpy") else seq_lens
+    pt = np.ascontiguousarray(np.asarray(pt, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(sl, dtype=np.int32))
+    B, H, d = q.shape
+    num_pages, H_kv, page_size, d2 = kc.shape
+    if d2 != d or vc.shape != kc.shape or pt.shape[0] != B or sl.shape != (B,):
+        raise ValueError("inconsistent decode shapes")
+    o = np.empty((B, H, d))
+    lse = np.empty((B, H))
+    ip = ctypes.POINTER(ctypes.c_int)
+    _check(_load().oracle_decode_paged(_ptr(q), _ptr(kc), _ptr(vc), pt.ctypes.data_as(ip),
+                                       sl.ctypes.data_as(ip), B, H, H_kv, d, num_pages,
+                                       page_size, pt.shape[1], float(scale), _ptr(o), _ptr(lse)),
+           "decode_paged")
+    return o, lse

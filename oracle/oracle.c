@@ -606,3 +606,80 @@ int oracle_decode_e4m3(const unsigned char *x, long n, double scale, double *out
     }
     return ORACLE_OK;
 }
+
+/*
+ * Decode-step attention over a paged KV cache: one new query token per
+ * sequence attends to all L_b cached tokens of its sequence, whose keys and
+ * values live in fixed-size pages located through a per-sequence page table
+ * (the KV-cache layout the pages point to as the next step, "PagedAttention:
+ * pages, page tables" in [P1, "What's Next?"]). The result is the definition
+ * of attention for that one row: token t of sequence b is page
+ * page_table[b][t / page_size], row t % page_size; then
+ *   s_t = scale * q . k_t,  P = softmax(s),  o = sum_t P_t v_t,
+ *   lse = ln sum_t exp(s_t),
+ * computed with attention_row on the gathered rows (no mask: the new token
+ * sees every cached token, itself included).
+ * q, o: [B][H][d]; k_cache, v_cache: [num_pages][H_kv][page_size][d];
+ * page_table: [B][max_pages]; seq_lens: [B]; lse: [B][H]. Query head h
+ * reads KV head h / (H / H_kv). Every L_b must be in [1, max_pages *
+ * page_size] and every page index used in [0, num_pages).
+ */
+int oracle_decode_paged(const double *q, const double *k_cache, const double *v_cache,
+                        const int *page_table, const int *seq_lens, long B, long H,
+                        long H_kv, long d, long num_pages, long page_size, long max_pages,
+                        double scale, double *o, double *lse)
+{
+    if (B < 0 || H < 1 || H_kv < 1 || H % H_kv || d < 1 || num_pages < 1 || page_size < 1 ||
+        max_pages < 1)
+        return ORACLE_ERR_ARG;
+    if (B == 0)
+        return ORACLE_OK;
+    if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o || !lse ||
+        !isfinite(scale))
+        return ORACLE_ERR_ARG;
+    long maxlen = 0;
+    for (long b = 0; b < B; ++b) {
+        const long L = seq_lens[b];
+        if (L < 1 || L > max_pages * page_size)
+            return ORACLE_ERR_ARG;
+        for (long t = 0; t < (L + page_size - 1) / page_size; ++t) {
+            const int pg = page_table[b * max_pages + t];
+            if (pg < 0 || pg >= num_pages)
+                return ORACLE_ERR_ARG;
+        }
+        if (L > maxlen)
+            maxlen = L;
+    }
+    int nt = oracle_num_threads();
+    const size_t per = (size_t)maxlen * (size_t)d * 2 + 2 * (size_t)maxlen;
+    double *scratch = (double *)malloc((size_t)nt * per * sizeof(double));
+    if (!scratch)
+        return ORACLE_ERR_NOMEM;
+    const long group = H / H_kv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (long b = 0; b < B; ++b)
+        for (long h = 0; h < H; ++h) {
+            int tid = 0;
+#ifdef _OPENMP
+            tid = omp_get_thread_num();
+#endif
+            double *K = scratch + (size_t)tid * per;
+            double *V = K + (size_t)maxlen * d;
+            double *S = V + (size_t)maxlen * d;
+            double *P = S + maxlen;
+            const long L = seq_lens[b], hk = h / group;
+            /* gather the sequence's rows of this KV head through the page table */
+            for (long t = 0; t < L; ++t) {
+                const long pg = page_table[b * max_pages + t / page_size];
+                const size_t src = (((size_t)pg * H_kv + hk) * page_size + t % page_size) * d;
+                memcpy(K + (size_t)t * d, k_cache + src, (size_t)d * sizeof(double));
+                memcpy(V + (size_t)t * d, v_cache + src, (size_t)d * sizeof(double));
+            }
+            const double *qh = q + ((size_t)b * H + h) * d;
+            /* one row of standard attention: query row 0 against L keys */
+            attention_row(qh, K, V, L, d, scale, 0, 0, S, P, o + ((size_t)b * H + h) * d,
+                          lse + (size_t)b * H + h);
+        }
+    free(scratch);
+    return ORACLE_OK;
+}
