@@ -48,18 +48,21 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k.json"),
                  "bwd": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_bwd.json"),
                  "std": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_std.json"),
-                 "fp8": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_fp8.json")}
+                 "fp8": os.path.join(ROOT, "profiles", "hbm_traffic_longdoc8k_fp8.json"),
+                 "decode": os.path.join(ROOT, "profiles", "hbm_traffic_decode50.json")}
 # Sources each pass's kernels are compiled from (the traffic summary is valid
 # only for the exact sources it was taken on).
 PASS_SOURCES = {"fwd": ("fa_common.h", "fa_lds.h", "fa_fwd_bf16.hip"),
                 "bwd": ("fa_common.h", "fa_lds.h", "fa_bwd_bf16.hip"),
                 "std": ("fa_common.h", "fa_std.hip"),
-                "fp8": ("fa_common.h", "fa_lds.h", "fa_fwd_fp8.hip")}
+                "fp8": ("fa_common.h", "fa_lds.h", "fa_fwd_fp8.hip"),
+                "decode": ("fa_common.h", "fa_decode.hip")}
 # Kernel names (substrings) rocprofv3 reports for each pass.
 PASS_KERNELS = {"fwd": ("fa_fwd_bf16_kernel",),
                 "bwd": ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"),
                 "std": ("fa_std_softmax",),
-                "fp8": ("fa_fwd_fp8_kernel",)}
+                "fp8": ("fa_fwd_fp8_kernel",),
+                "decode": ("fa_decode_split_kernel", "fa_decode_merge_kernel")}
 
 
 def log(*a):
@@ -205,17 +208,113 @@ def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
     }
 
 
+def bench_decode(args):
+    """One step = one fa_decode_paged call (split + merge kernels) over the
+    paged KV cache of a decode workload; value = algorithmic HBM bytes (every
+    cached K and V row read once, q, o, lse) / time, in GB/s."""
+    import torch
+    import io_aware_tiled_09_amd as fa
+    from io_aware_tiled_09_amd.inputs import DECODE_WORKLOADS, decode_kv_bytes, make_decode
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 3
+    fa.load()
+    name = args.workload if args.workload in DECODE_WORKLOADS else "decode50"
+    x = make_decode(name)
+    w = x["workload"]
+    dev = torch.device("cuda:0")
+    g = {k: x[k].to(dev) for k in ("q", "k_cache", "v_cache", "page_table", "seq_lens")}
+    log(f"decode workload {name}: B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} page_size={w.page_size} "
+        f"pages={g['k_cache'].shape[0]} mean len={float(x['seq_lens'].float().mean()):.0f}")
+    need = fa.fa_decode_workspace_bytes(w.B, w.H, w.d, w.page_size, w.max_pages)
+    ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    o = torch.empty_like(g["q"])
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    num_pages = g["k_cache"].shape[0]
+
+    def step():
+        st = fa.fa_decode_paged(g["q"], g["k_cache"], g["v_cache"], g["page_table"],
+                                g["seq_lens"], o, lse, ws, need, w.B, w.H, w.H_kv, w.d,
+                                num_pages, w.page_size, w.max_pages, w.scale, stream)
+        if st != 0:
+            raise fa.FAError(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg_ms = sum(per) / K
+    span_ms = starts[0].elapsed_time(ends[-1]) / K
+    nbytes = decode_kv_bytes(w, x["seq_lens"])
+    value = nbytes / (span_ms * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    log(f"avg call {avg_ms:.4f} ms, span/step {span_ms:.4f} ms, {nbytes / 1e9:.3f} GB -> "
+        f"{value:.0f} GB/s")
+    digest = kernel_source_digest("decode")
+    result = {
+        "metric": "decode-step attention over a paged KV cache, GB/s of cache read (bf16, 1 MI355X)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(span_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "d": w.d,
+                   "page_size": w.page_size, "max_context": w.max_context,
+                   "tokens": int(x["seq_lens"].sum()), "seed": w.seed,
+                   "algorithmic_bytes": nbytes, "pass": "decode"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(digest, "decode"),
+                     "avg_launch_ms": round(avg_ms, 5),
+                     "kernels": list(PASS_KERNELS["decode"]), "kernel_source_digest": digest},
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["page_table"], x["seq_lens"],
+                            w.scale)
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": nbytes / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the whole step ({w.B} sequences, {int(x['seq_lens'].sum())} tokens) "
+                      f"in fp64, {el:.1f} s wall including the fp64 upcast of the cache"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="longdoc8k")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "std", "fp8"), default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "std", "fp8", "decode"),
+                    default="fwd",
                     help="fwd: one step = one forward call (the default line); bwd: one "
                          "step = one backward call (fa_bwd) given O and lse; std: one step = "
                          "the standard materializing forward (S and P through HBM); fp8: one "
-                         "step = one FP8 (E4M3) forward call (fa_fwd_fp8)")
+                         "step = one FP8 (E4M3) forward call (fa_fwd_fp8); decode: one step = "
+                         "one decode step over a paged KV cache (fa_decode_paged, --workload "
+                         "decode50 by default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
@@ -236,6 +335,9 @@ def main(argv=None):
               "multi-GPU path (each (batch, head) is independent; see the sharding "
               "notes in the design document).", file=sys.stderr)
         return 2
+
+    if args.pass_ == "decode":
+        return bench_decode(args)
 
     import torch
     import io_aware_tiled_09_amd as fa

@@ -35,6 +35,8 @@
 #ifndef IO_AWARE_TILED_09_FA_H
 #define IO_AWARE_TILED_09_FA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -121,6 +123,36 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
 int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                int B, int H, int N, int d, float scale, float q_scale,
                float k_scale, float v_scale, int causal, void *stream);
+
+/*
+ * Decode-step attention over a paged KV cache: for each sequence b one new
+ * query token (q[b][h]) attends to the sequence's seq_lens[b] cached tokens.
+ * Token t of sequence b is row t % page_size of physical page
+ * page_table[b][t / page_size]; query head h reads KV head h / (H / H_kv).
+ * o[b][h] = sum_t softmax_t(scale * q . k_t) v_t and lse[b][h] = ln sum_t
+ * exp(scale * q . k_t) (natural log); the new token's own K and V are
+ * expected in the cache already (no mask).
+ * [FlashAttention: The GPU Memory Hack That Changed Everything
+ *  (ai.branddocks.com, episode 75), "What's Next?": PagedAttention's pages
+ *  and page tables for the KV cache]
+ * q, o: bf16 [B][H][d]; k_cache, v_cache: bf16 [num_pages][H_kv][page_size]
+ * [d] (16-byte aligned); page_table: int32 [B][max_pages]; seq_lens: int32
+ * [B]; lse: fp32 [B][H]; ws: fp32 workspace of at least
+ * fa_decode_workspace_bytes(B, H, d, page_size, max_pages) bytes, 16-byte
+ * aligned, contents overwritten. d in {64, 128}; H / H_kv in {1, 2, 4, 8};
+ * page_size a positive multiple of 16; scale >= 0 and finite.
+ * Device-side values are not checked on the host; the kernels clamp
+ * seq_lens[b] to max_pages * page_size, treat tokens whose page entry is
+ * outside [0, num_pages) as absent (weight 0, never read), and a sequence
+ * with no token gets o = 0 and lse = -inf. Rows of the cache that no
+ * sequence owns are never used, whatever they hold.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int page_size, int max_pages);
+int fa_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                    const int *page_table, const int *seq_lens, void *o, float *lse,
+                    void *ws, size_t ws_bytes, int B, int H, int H_kv, int d,
+                    int num_pages, int page_size, int max_pages, float scale,
+                    void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_string(int status);

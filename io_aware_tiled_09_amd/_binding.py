@@ -21,8 +21,8 @@ STATUS_NAMES = {
     4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_MISALIGNED", 6: "FA_ERR_ALIASING", 7: "FA_ERR_LAUNCH",
     8: "FA_ERR_TOO_LARGE", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_LIBRARY",
 }
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_status_string", "fa_tile_rows",
-           "fa_tile_cols")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_decode_paged",
+           "fa_decode_workspace_bytes", "fa_status_string", "fa_tile_rows", "fa_tile_cols")
 
 
 class FAError(RuntimeError):
@@ -48,6 +48,10 @@ def load():
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, f, f, f, i, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_decode_paged.argtypes = [vp] * 8 + [ctypes.c_size_t] + [i] * 7 + [f, vp]
+    lib.fa_decode_paged.restype = i
     lib.fa_bwd.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -109,6 +113,21 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, d, scale, causal, str
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), int(B), int(H), int(N),
                              int(d), float(scale), int(bool(causal)),
                              _stream(stream, (q, k, v, o, lse, dout))))
+
+
+def fa_decode_workspace_bytes(B, H, d, page_size, max_pages) -> int:
+    return int(load().fa_decode_workspace_bytes(int(B), int(H), int(d), int(page_size),
+                                                int(max_pages)))
+
+
+def fa_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse, ws, ws_bytes, B, H, H_kv,
+                    d, num_pages, page_size, max_pages, scale, stream=None) -> int:
+    """C fa_decode_paged (see include/fa.h). Returns the fa_status code."""
+    return int(load().fa_decode_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _ptr(o),
+        _ptr(lse), _ptr(ws), int(ws_bytes), int(B), int(H), int(H_kv), int(d), int(num_pages),
+        int(page_size), int(max_pages), float(scale),
+        _stream(stream, (q, k_cache, v_cache, o, lse))))
 
 
 def fa_status_string(status: int) -> str:
@@ -195,6 +214,37 @@ def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=Non
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     st = fa_fwd_fp8(q8, k8, v8, o, lse, B, H, N, d, scale, q_scale, k_scale, v_scale, causal,
                     stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse
+
+
+def decode_paged(q, k_cache, v_cache, page_table, seq_lens, scale=None, ws=None, stream=None):
+    """Allocate o, lse (and the workspace unless given) with torch and run one
+    decode step over the paged KV cache. q: bf16 [B, H, d]; caches: bf16
+    [num_pages, H_kv, page_size, d]; page_table: int32 [B, max_pages];
+    seq_lens: int32 [B]; all contiguous CUDA tensors. Returns (o, lse)."""
+    import torch
+    B, H, d = q.shape
+    num_pages, H_kv, page_size, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or page_table.dim() != 2 or \
+            page_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("inconsistent decode shapes")
+    for t, dt in ((q, torch.bfloat16), (k_cache, torch.bfloat16), (v_cache, torch.bfloat16),
+                  (page_table, torch.int32), (seq_lens, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("decode inputs must be contiguous CUDA tensors of the stated dtypes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    max_pages = page_table.shape[1]
+    need = fa_decode_workspace_bytes(B, H, d, page_size, max_pages)
+    if ws is None:
+        ws = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    st = fa_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse, ws,
+                         ws.numel() * ws.element_size(), B, H, H_kv, d, num_pages, page_size,
+                         max_pages, scale, stream)
     if st != FA_OK:
         raise FAError(st)
     return o, lse

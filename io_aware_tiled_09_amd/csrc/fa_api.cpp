@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/fa.h"
@@ -131,6 +132,65 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     const float c_log2 = c < FLT_MIN ? FLT_MIN : (float)c;
     const hipError_t e = fa::launch_fp8(q, k, v, o, lse, B * H, N, c_log2, v_scale, causal != 0,
                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int page_size, int max_pages)
+{
+    if (B < 1 || H < 1 || d < 1 || page_size < 1 || max_pages < 1)
+        return 0;
+    return (size_t)B * (size_t)H * (size_t)fa::decode_max_splits(max_pages, page_size) *
+           (size_t)(d + 2) * sizeof(float);
+}
+
+int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                    const int* page_table, const int* seq_lens, void* o, float* lse, void* ws,
+                    size_t ws_bytes, int B, int H, int H_kv, int d, int num_pages, int page_size,
+                    int max_pages, float scale, void* stream)
+{
+    if (B < 0 || H < 1 || H_kv < 1 || num_pages < 1 || page_size < 1 || max_pages < 1 ||
+        H % H_kv != 0 || page_size % 16 != 0)
+        return FA_ERR_BAD_SHAPE;
+    const int G = H / H_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return FA_ERR_BAD_SHAPE;
+    if (B == 0)
+        return FA_OK;
+    if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o || !lse)
+        return FA_ERR_NULL_PTR;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!isfinite(scale) || scale < 0.0f)
+        return FA_ERR_BAD_SCALE;
+    if (B > 65535 || H_kv > 65535 || H > 65535 ||
+        (long long)max_pages * page_size > 0x7fffffffLL)
+        return FA_ERR_TOO_LARGE;
+    const size_t need = fa_decode_workspace_bytes(B, H, d, page_size, max_pages);
+    auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
+    if (!ws || (addr(ws) & 15u) || ws_bytes < need)
+        return FA_ERR_WORKSPACE;
+    if ((addr(q) | addr(k_cache) | addr(v_cache) | addr(o)) & 15u ||
+        (addr(page_table) | addr(seq_lens) | addr(lse)) & 3u)
+        return FA_ERR_MISALIGNED;
+    const uintptr_t qb = (uintptr_t)B * H * d * 2, cb = (uintptr_t)num_pages * H_kv * page_size * d * 2;
+    const Range in[5] = {{addr(q), addr(q) + qb}, {addr(k_cache), addr(k_cache) + cb},
+                         {addr(v_cache), addr(v_cache) + cb},
+                         {addr(page_table), addr(page_table) + (uintptr_t)B * max_pages * 4},
+                         {addr(seq_lens), addr(seq_lens) + (uintptr_t)B * 4}};
+    const Range out[3] = {{addr(o), addr(o) + qb}, {addr(lse), addr(lse) + (uintptr_t)B * H * 4},
+                          {addr(ws), addr(ws) + need}};
+    for (int x = 0; x < 3; ++x) {
+        for (int y = 0; y < 5; ++y)
+            if (overlaps(out[x], in[y]))
+                return FA_ERR_ALIASING;
+        for (int y = x + 1; y < 3; ++y)
+            if (overlaps(out[x], out[y]))
+                return FA_ERR_ALIASING;
+    }
+    const hipError_t e = fa::launch_decode(q, k_cache, v_cache, page_table, seq_lens, o, lse,
+                                           static_cast<float*>(ws), B, H, H_kv, d, num_pages,
+                                           page_size, max_pages, kernel_scale(scale),
+                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

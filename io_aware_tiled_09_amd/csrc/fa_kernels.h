@@ -28,4 +28,18 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
 hipError_t launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                       int N, float c_log2, float out_scale, bool causal, hipStream_t stream);
 
+// Decode over a paged KV cache. Keys per split workgroup, and the number of
+// split slots per (sequence, head) in the workspace.
+constexpr int kSplit = 256;
+inline int decode_max_splits(int max_pages, int page_size) {
+    return (int)(((long long)max_pages * page_size + kSplit - 1) / kSplit);
+}
+// q, o: bf16 [B][H][d]; caches: bf16 [num_pages][H_kv][page_size][d];
+// ws: fp32 workspace of B*H*max_splits*(d + 2) floats; c_log2 = scale*log2(e).
+// Validated: d in {64, 128}, H / H_kv in {1, 2, 4, 8}, page_size % 16 == 0.
+hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int* page_table, const int* seq_lens, void* o, float* lse,
+                         float* ws, int B, int H, int H_kv, int d, int num_pages, int page_size,
+                         int max_pages, float c_log2, hipStream_t stream);
+
 }  // namespace fa

@@ -103,6 +103,40 @@ def test_fp8_argument_errors():
         assert fa.fa_fwd_fp8(None, None, None, None, None, B, H, N, 128, 0.1, 1, 1, 1, 1, None) == 0
 
 
+def _dec(q=A, kc=A + 64 * MB, vc=A + 128 * MB, pt=A + 192 * MB, sl=A + 193 * MB, o=A + 194 * MB,
+         lse=A + 195 * MB, ws=A + 196 * MB, ws_bytes=None, B=3, H=8, H_kv=2, d=128,
+         num_pages=40, page_size=16, max_pages=10, scale=0.1):
+    if ws_bytes is None:
+        ws_bytes = fa.fa_decode_workspace_bytes(B, H, d, page_size, max_pages)
+    return fa.fa_decode_paged(q, kc, vc, pt, sl, o, lse, ws, ws_bytes, B, H, H_kv, d, num_pages,
+                              page_size, max_pages, scale, 0)
+
+
+def test_decode_workspace_bytes():
+    # B * H * ceil(max_pages * page_size / 256) slots of (d + 2) floats
+    assert fa.fa_decode_workspace_bytes(3, 8, 128, 16, 10) == 3 * 8 * 1 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(50, 32, 128, 16, 512) == 50 * 32 * 32 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(0, 8, 128, 16, 10) == 0
+
+
+def test_decode_argument_errors():
+    assert _dec(pt=0) == 1
+    assert _dec(H=8, H_kv=3) == 2           # H not a multiple of H_kv
+    assert _dec(H=32, H_kv=2) == 2          # 16 query heads per KV head: not built
+    assert _dec(page_size=24) == 2          # not a multiple of 16
+    assert _dec(num_pages=0) == 2
+    assert _dec(d=96) == 3
+    assert _dec(scale=-1.0) == 4
+    assert _dec(kc=A + 64 * MB + 8) == 5
+    assert _dec(sl=A + 193 * MB + 2) == 5
+    assert _dec(ws_bytes=100) == 9
+    assert _dec(ws=0) == 9
+    assert _dec(o=A + 64 * MB) == 6         # o over the K cache
+    assert _dec(ws=A + 128 * MB) == 6       # workspace over the V cache
+    assert _dec(B=70000) == 8
+    assert fa.fa_decode_paged(*([None] * 8), 0, 0, 8, 2, 128, 4, 16, 4, 0.1, None) == 0
+
+
 def _bwd(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
          dout=A + 320 * MB, dq=A + 384 * MB, dk=A + 448 * MB, dv=A + 512 * MB, ws=A + 576 * MB,
          B=1, H=2, N=100, d=64, scale=0.125, causal=0):
