@@ -261,6 +261,14 @@ def bench_decode(args):
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
     log(f"avg call {avg_ms:.4f} ms, span/step {span_ms:.4f} ms, {nbytes / 1e9:.3f} GB -> "
         f"{value:.0f} GB/s")
+    if args.copy_kernel_mib > 0:
+        n = args.copy_kernel_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy kernel: {args.copy_kernel_mib} MiB read + written, 3 times")
     digest = kernel_source_digest("decode")
     result = {
         "metric": "decode-step attention over a paged KV cache, GB/s of cache read (bf16, 1 MI355X)",

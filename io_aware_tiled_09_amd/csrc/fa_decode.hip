@@ -9,11 +9,11 @@
 // once and is bound by HBM bandwidth, so the design is about streaming.
 //
 // Two kernels, no atomics:
-//  * split: one workgroup of 256 threads per (sequence, KV head, run of
-//    kSplit keys). The 16 lane-groups of 16 lanes each take one key of every
-//    16-key row block of a page (one page-table entry per block, so each
-//    block is 16 consecutive rows: coalesced 16-byte loads), kUnroll blocks
-//    at a time with all loads issued first. A group keeps, for each of the G
+//  * split: kRunGroups workgroups of 256 threads per (sequence, KV head),
+//    each taking every kRunGroups-th run of kSplit keys. The run's page-table entries are looked up once into LDS.
+//    The 16 lane-groups of 16 lanes each take one key of every 16-key row
+//    block of a page (16 consecutive rows: coalesced 16-byte loads), kUnroll
+//    blocks at a time with all loads issued first. A group keeps, for each of the G
 //    query heads that share the KV head, the online-softmax state of its keys
 //    (running max m, sum l, and its d/16 slice of the weighted V sum). The
 //    16 group states are merged (within a wave by lane shuffles, across the
@@ -35,7 +35,8 @@ namespace fa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kUnroll = 4;                  // row blocks in flight per group
+constexpr int kBlocks = kSplit / 16;        // 16-row blocks per run
+constexpr int kRunGroups = 4;               // workgroups per (sequence, KV head)
 
 struct DecodeArgs {
     const __bf16* q;
@@ -65,11 +66,14 @@ __device__ inline void merge_state(float& m, float& l, float* acc, int n, float 
 template <int D, int G>
 __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodeArgs a)
 {
-    constexpr int E = D / 16;  // d-elements per lane
-    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    constexpr int E = D / 16;                    // d-elements per lane
+    constexpr int kUnroll = G <= 2 ? 8 : 4;      // row blocks in flight per group
+    const int hk = blockIdx.y, b = blockIdx.z;
     const int L = min(a.seq_lens[b], a.max_pages * a.page_size);
+    // Workgroup x takes runs x, x + gridDim.x, ... of its (sequence, KV head):
+    // a short sequence leaves few workgroups idle, a long one is still spread.
+    for (int split = blockIdx.x; split * kSplit < L; split += gridDim.x) {
     const int j_begin = split * kSplit;
-    if (j_begin >= L) return;  // uniform: this workgroup has no keys
     const int j_end = min(L, j_begin + kSplit);
 
     const int tid = threadIdx.x;
@@ -77,6 +81,20 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodeArgs
     const int wave = tid >> 6;
     const int grp = tid >> 4;    // 0..15: the key of each 16-row block
     const int e0 = (tid & 15) * E;
+
+    // The run's first row of every 16-row block, as an element offset into
+    // the caches (or -1: past the end or an unmapped page), looked up once.
+    __shared__ long long blk_row[kBlocks];
+    if (tid < kBlocks) {
+        const int blk = j_begin + tid * 16;
+        long long r = -1;
+        if (blk < j_end) {
+            const int pg = a.page_table[(size_t)b * a.max_pages + blk / a.page_size];
+            if (pg >= 0 && pg < a.num_pages)
+                r = (((long long)pg * a.H_kv + hk) * a.page_size + blk % a.page_size) * D;
+        }
+        blk_row[tid] = r;
+    }
 
     // This lane's slice of each of the G query rows, fp32.
     float qv[G][E];
@@ -94,29 +112,22 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodeArgs
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
     }
+    __syncthreads();  // blk_row is ready
 
-    const int* table = a.page_table + (size_t)b * a.max_pages;
-    const size_t head_rows = (size_t)a.page_size;            // rows of one (page, KV head)
-    const size_t page_stride = (size_t)a.H_kv * head_rows;  // rows of one page
-
-    for (int jb = j_begin; jb < j_end; jb += 16 * kUnroll) {
+    const int nblk = (j_end - j_begin + 15) / 16;
+    for (int bb = 0; bb < nblk; bb += kUnroll) {
         // Issue every load of kUnroll row blocks first.
         typedef __bf16 bfE __attribute__((ext_vector_type(E)));
         bfE kr[kUnroll], vr[kUnroll];
         bool ok[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int j = jb + u * 16 + grp;
-            const int blk = jb + u * 16;  // 16-aligned, inside one page
-            const int pg = blk < j_end ? table[blk / a.page_size] : -1;
-            ok[u] = j < j_end && pg >= 0 && pg < a.num_pages;
-            const size_t row = ok[u] ? ((size_t)pg * page_stride + (size_t)hk * head_rows +
-                                        (size_t)(j % a.page_size))
-                                     : 0;
-            const __bf16* kp = a.k_cache + row * D + e0;
-            const __bf16* vp = a.v_cache + row * D + e0;
-            kr[u] = ok[u] ? *reinterpret_cast<const bfE*>(kp) : bfE{};
-            vr[u] = ok[u] ? *reinterpret_cast<const bfE*>(vp) : bfE{};
+            const int blk = bb + u;
+            const long long r0 = blk < nblk ? blk_row[blk] : -1;
+            ok[u] = r0 >= 0 && j_begin + blk * 16 + grp < j_end;
+            const size_t off = ok[u] ? (size_t)r0 + (size_t)grp * D + e0 : 0;
+            kr[u] = ok[u] ? *reinterpret_cast<const bfE*>(a.k_cache + off) : bfE{};
+            vr[u] = ok[u] ? *reinterpret_cast<const bfE*>(a.v_cache + off) : bfE{};
         }
         // Scores of the group's kUnroll keys for each query head.
 #pragma unroll
@@ -191,6 +202,8 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodeArgs
             a.ws_ml[slot * 2 + 1] = ll;
         }
     }
+    __syncthreads();  // the LDS arrays are reused by the next run
+    }
 }
 
 template <int D>
@@ -229,7 +242,7 @@ __global__ __launch_bounds__(64) void fa_decode_merge_kernel(DecodeArgs a)
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeArgs& a, int B, hipStream_t stream)
 {
-    hipLaunchKernelGGL((fa_decode_split_kernel<D, G>), dim3(a.max_splits, a.H_kv, B),
+    hipLaunchKernelGGL((fa_decode_split_kernel<D, G>), dim3(min(a.max_splits, kRunGroups), a.H_kv, B),
                        dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL((fa_decode_merge_kernel<D>), dim3(a.H, B), dim3(64), 0, stream, a);
     return hipGetLastError();

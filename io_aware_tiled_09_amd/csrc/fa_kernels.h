@@ -30,7 +30,7 @@ hipError_t launch_fp8(const void* q, const void* k, const void* v, void* o, floa
 
 // Decode over a paged KV cache. Keys per split workgroup, and the number of
 // split slots per (sequence, head) in the workspace.
-constexpr int kSplit = 256;
+constexpr int kSplit = 512;
 inline int decode_max_splits(int max_pages, int page_size) {
     return (int)(((long long)max_pages * page_size + kSplit - 1) / kSplit);
 }

@@ -113,9 +113,9 @@ def _dec(q=A, kc=A + 64 * MB, vc=A + 128 * MB, pt=A + 192 * MB, sl=A + 193 * MB,
 
 
 def test_decode_workspace_bytes():
-    # B * H * ceil(max_pages * page_size / 256) slots of (d + 2) floats
+    # B * H * ceil(max_pages * page_size / 512) slots of (d + 2) floats
     assert fa.fa_decode_workspace_bytes(3, 8, 128, 16, 10) == 3 * 8 * 1 * 130 * 4
-    assert fa.fa_decode_workspace_bytes(50, 32, 128, 16, 512) == 50 * 32 * 32 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(50, 32, 128, 16, 512) == 50 * 32 * 16 * 130 * 4
     assert fa.fa_decode_workspace_bytes(0, 8, 128, 16, 10) == 0
 
 

@@ -3,7 +3,7 @@ through the C ABI) against the fp64 oracle (oracle.decode_paged).
 
 Bound, per element, from the kernel's arithmetic: bf16 inputs, exact
 products summed in fp32, an fp32 online softmax and fp32 accumulation of the
-weighted V rows (the partial states of 16-key groups and 256-key runs merged
+weighted V rows (the partial states of 16-key groups and 512-key runs merged
 with the two-correction-factor merge), O rounded to bf16:
     |O_gpu - O| <= 2^-8 |O| + 2^-12 A + 1e-6,  A_t = sum_j P_j |V_jt|
 (2^-8: the bf16 rounding of O; 2^-12 A: fp32 summation over up to 8K terms,
@@ -60,10 +60,10 @@ def test_decode_small(d, H, H_kv, page_size):
 
 
 def test_decode_split_boundaries():
-    """Lengths around the 16-key row blocks, the 64-key unrolled step and the
-    256-key runs."""
+    """Lengths around the 16-key row blocks, the unrolled steps (64 and 128
+    keys) and the 512-key runs."""
     say("decode split boundaries")
-    lens = [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1023, 1024]
+    lens = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1023, 1024]
     x = make_decode("decode_small", B=len(lens), H=4, H_kv=4, seed=7, max_context=1024)
     w = x["workload"]
     x["seq_lens"] = torch.tensor(lens, dtype=torch.int32)
