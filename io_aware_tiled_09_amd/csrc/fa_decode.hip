@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kBlocks = kSplit / 16;        // 16-row blocks per run
-constexpr int kRunGroups = 4;               // workgroups per (sequence, KV head)
+constexpr int kRunGroups = 3;               // workgroups per (sequence, KV head)
 
 struct DecodeArgs {
     const __bf16* q;
