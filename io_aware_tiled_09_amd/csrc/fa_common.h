@@ -60,7 +60,7 @@ template <bool MASKED, int NT>
 __device__ inline float probs(const f32x16 (&s)[kBc / 32], float c, float m,
                               bf16x8 (&pf)[NT][kBc / 32][2])
 {
-    float lsum = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
 #pragma unroll
     for (int st = 0; st < kBc / 32; ++st)
 #pragma unroll
@@ -70,12 +70,12 @@ __device__ inline float probs(const f32x16 (&s)[kBc / 32], float c, float m,
                 const float x = s[st][h2 * 8 + r];
                 float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m));
                 if (MASKED) p = x > neg_inf() ? p : 0.f;
-                lsum += p;
+                ls[r & 3] += p;
                 const __bf16 ph = (__bf16)p;
                 pf[0][st][h2][r] = ph;
                 if constexpr (NT == 2) pf[1][st][h2][r] = (__bf16)(p - (float)ph);
             }
-    return lsum;
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
 // Work split over (batch*head, query block).

@@ -268,11 +268,12 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     auto phase_a = [&](int kb) __attribute__((always_inline)) {
         if (kb > last) return;
         if (kb >= nfull_w) mask(kb, sc);
-        float mraw = neg_inf();
+        float mr4[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
 #pragma unroll
         for (int st = 0; st < kBc / 32; ++st)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, sc[st][r]);
+            for (int r = 0; r < 16; ++r) mr4[r & 3] = fmaxf(mr4[r & 3], sc[st][r]);
+        float mraw = fmaxf(fmaxf(mr4[0], mr4[1]), fmaxf(mr4[2], mr4[3]));
         mraw = max_with_partner(mraw);
         // scale >= 0, so the scaled max is scale_log2 * raw max
         const float mtile = mraw > neg_inf() ? mraw * scale_log2 : neg_inf();
