@@ -93,13 +93,22 @@ def measured_traffic(digest: str, pass_: str = "fwd"):
 
 
 def _counter_means(path, counter):
+    """Mean counter value per kernel name, over the dispatches with that
+    kernel's largest grid (so that the 1 GiB calibration copy is not averaged
+    with small runtime copies of the same blit kernel)."""
     import csv
     by_kernel = {}
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter:
-                by_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    return {k_: sum(v_) / len(v_) for k_, v_ in by_kernel.items()}
+                by_kernel.setdefault(r["Kernel_Name"], []).append(
+                    (int(r.get("Grid_Size") or 0), float(r["Counter_Value"])))
+    out = {}
+    for k_, v_ in by_kernel.items():
+        g = max(x[0] for x in v_)
+        vals = [x[1] for x in v_ if x[0] == g]
+        out[k_] = sum(vals) / len(vals)
+    return out
 
 
 def ingest_counters(fetch_csv, write_csv, copy_mib, command, pass_="fwd"):
@@ -131,7 +140,7 @@ def ingest_counters(fetch_csv, write_csv, copy_mib, command, pass_="fwd"):
     traffic = (fetch_kib * f_fetch + write_kib * f_write) * 1024.0
     out = {
         "kernel_source_digest": kernel_source_digest(pass_),
-        "workload": "longdoc8k",
+        "workload": "decode50" if pass_ == "decode" else "longdoc8k",
         "pass": pass_,
         "hbm_bytes_per_launch": round(traffic),
         "fetch_kib_raw": fetch_kib,
