@@ -86,7 +86,7 @@ struct Tile8 {
 };
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(CAUSAL ? 3 : 2, CAUSAL ? 3 : 2)))
 void fa_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                        const uint8_t* __restrict__ v, __bf16* __restrict__ o,
                        float* __restrict__ lse, int BH, int N, int nqb, float c_log2,
