@@ -1,7 +1,10 @@
 /*
- * fa.h: C ABI of the FlashAttention forward library (libfa.so, gfx950).
+ * fa.h: C ABI of the FlashAttention library (libfa.so, gfx950): the forward
+ * pass (bf16 storage, fp32 storage, FP8 inputs), the backward pass, and
+ * decode-step attention over a paged KV cache. The standard, materializing
+ * baseline has its own library and header (fa_std.h).
  *
- * The operation is exact softmax attention for every (batch, head):
+ * The forward operation is exact softmax attention for every (batch, head):
  *
  *     S = scale * Q K^T          (N x N, never stored)
  *     P = softmax(S) row-wise    (causal: key j visible to query i iff j <= i)
@@ -17,10 +20,11 @@
  * [same first page, "Integration": is_causal]
  *
  * Layout: q, k, v and o are contiguous row-major [B][H][N][d]; lse is
- * contiguous [B][H][N] fp32. All five pointers are DEVICE pointers on the
- * current HIP device. The caller allocates and frees every buffer; the
- * library allocates nothing, frees nothing, keeps no state between calls and
- * does not synchronize.
+ * contiguous [B][H][N] fp32 (the decode entry point documents its own
+ * layout). Every pointer is a DEVICE pointer on the current HIP device. The
+ * caller allocates and frees every buffer, workspaces included; the library
+ * allocates nothing, frees nothing, keeps no state between calls and does
+ * not synchronize.
  *
  * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL means the
  * default stream) and the call returns once it is launched. Results are
