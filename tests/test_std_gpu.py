@@ -9,7 +9,7 @@ with V, and O is rounded to bf16 (<= 2^-8 |O|). So, to first order,
     |O_gpu - O| <= 2^-8 (sum_j P_ij |V_jt| + |O_it|),
 and the test allows 1.05 times that plus 1e-5, with sum_j P_ij |V_jt| from
 the oracle run on |V|. (The flash path's dominant weight is an unnormalized
-exp2(0) = 1, exact in bf16, which is why the benchmark spec's bound of 2e-2 holds
+exp2(0) = 1, exact in bf16, which is why the flash bound of 2e-2 holds
 there even on spiky rows while it need not here.) Mean |dO| <= 2e-3 and lse
 as the flash path (tests/_parity.py)."""
 import math
