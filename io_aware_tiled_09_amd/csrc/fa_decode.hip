@@ -9,8 +9,13 @@
 // once and is bound by HBM bandwidth, so the design is about streaming.
 //
 // Two kernels, no atomics:
-//  * split: kRunGroups workgroups of 256 threads per (sequence, KV head),
-//    each taking every kRunGroups-th run of kSplit keys. The run's page-table entries are looked up once into LDS.
+//  * split: kRunGroups * G workgroups of 256 threads per (sequence, KV
+//    head), each taking every (kRunGroups * G)-th run of kSplit keys. With G
+//    query heads per KV head there are G times fewer (sequence, KV head)
+//    pairs and G times the arithmetic per row, so G times the workgroups keep
+//    as many rows in flight (measured on 50 sequences, H = 32, H_kv = 8:
+//    3.6 TB/s against 3.1 with 3; 4 * G or one per run: 2.0). The run's
+//    page-table entries are looked up once into LDS.
 //    The 16 lane-groups of 16 lanes each take one key of every 16-key row
 //    block of a page (16 consecutive rows: coalesced 16-byte loads), kUnroll
 //    blocks at a time with all loads issued first. A group keeps, for each of the G
@@ -36,7 +41,7 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kBlocks = kSplit / 16;        // 16-row blocks per run
-constexpr int kRunGroups = 3;               // workgroups per (sequence, KV head)
+constexpr int kRunGroups = 3;               // workgroups per (sequence, KV head) and query head of it
 
 struct DecodeArgs {
     const __bf16* q;
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(64) void fa_decode_merge_kernel(DecodeArgs a)
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeArgs& a, int B, hipStream_t stream)
 {
-    hipLaunchKernelGGL((fa_decode_split_kernel<D, G>), dim3(min(a.max_splits, kRunGroups), a.H_kv, B),
+    hipLaunchKernelGGL((fa_decode_split_kernel<D, G>), dim3(min(a.max_splits, kRunGroups * G), a.H_kv, B),
                        dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL((fa_decode_merge_kernel<D>), dim3(a.H, B), dim3(64), 0, stream, a);
     return hipGetLastError();
