@@ -39,6 +39,12 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * 64;
 constexpr int kBwdRows = kBwdWaves * 32;     // queries (dq) or keys (dkdv) per workgroup
+// __builtin_amdgcn_sched_group_barrier instruction classes, and how many MFMAs
+// ahead of their use the dq kernel's LDS fragment reads are issued (2, 4 and 6
+// measured within 0.3%; more would not fit the VGPR budget).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kDqReadAhead = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- delta
@@ -401,14 +407,12 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     int ld_off[L];
 #pragma unroll
     for (int it = 0; it < L; ++it) ld_off[it] = TL::load_offset(wave, it, lane);
-    int f_off[D / 16];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) f_off[c] = TL::frag_offset(li, 2 * c + lh);
-    int t_off[D / 32][2];
-#pragma unroll
-    for (int tt = 0; tt < D / 32; ++tt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) t_off[tt][s] = TL::tr_offset(tt, s, lane);
+    // Fragment offsets of chunk c and column block tt differ from those of
+    // c = 0 and tt = 0 only in bits 5-7 and 6-7 (the swizzle permutes chunk
+    // indices by XOR): f(c) = f(0) ^ (c << 5), t(tt, s) = t(0, s) ^ (tt << 6).
+    // Only the base offsets stay live; the rest are rebuilt per tile.
+    int f_base = TL::frag_offset(li, lh);
+    int t_base[2] = {TL::tr_offset(0, 0, lane), TL::tr_offset(0, 1, lane)};
 
     const int nkb_all = (N + kBc - 1) / kBc;
     const int nkb = CAUSAL ? min(nkb_all, (q0 + kBwdRows - 1) / kBc + 1) : nkb_all;
@@ -434,6 +438,7 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         if (active) {
             const unsigned char* kt = kbuf[b];
             const unsigned char* vt = vbuf[b];
+            asm volatile("" : "+v"(f_base), "+v"(t_base[0]), "+v"(t_base[1]));
             // S^T = K Q^T and dP^T = V dO^T: lane = query, 16 keys per sub-tile.
             f32x16 s[kBc / 32], dp[kBc / 32];
 #pragma unroll
@@ -442,28 +447,44 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 dp[st] = f32x16{};
 #pragma unroll
                 for (int c = 0; c < D / 16; ++c) {
-                    const int off = st * 32 * TL::kRowBytes + f_off[c];
+                    const int off = st * 32 * TL::kRowBytes + (f_base ^ (c << 5));
                     const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
                     const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + off);
                     s[st] = mfma(ka, qf[c], s[st]);
                     dp[st] = mfma(va, df[c], dp[st]);
                 }
             }
-            const bool need_mask = (CAUSAL && kb * kBc + kBc - 1 > qw0) || kb * kBc + kBc > N;
+            // K and V fragments a few MFMAs ahead, no further (VGPR budget).
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDqReadAhead, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * kBc / 32 * D / 16 - kDqReadAhead; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kDqReadAhead, 0);
+            // dS = P * (dP - D) as bf16 B operands; the mask is a separate
+            // code path so that unmasked tiles carry no compares or branches.
             bf16x8 dsf[kBc / 32][2];
+            auto make_ds = [&](auto masked) __attribute__((always_inline)) {
+                constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-            for (int st = 0; st < kBc / 32; ++st)
+                for (int st = 0; st < kBc / 32; ++st)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], scale_log2, -lse2));
-                    if (need_mask) {
-                        const int j = kb * kBc + score_key(st, r, lh);
-                        const bool ok = j < N && (!CAUSAL || j <= qi);
-                        p = ok ? p : 0.f;
+                    for (int r = 0; r < 16; ++r) {
+                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], scale_log2, -lse2));
+                        if constexpr (MASKED) {
+                            const int j = kb * kBc + score_key(st, r, lh);
+                            const bool ok = j < N && (!CAUSAL || j <= qi);
+                            p = ok ? p : 0.f;
+                        }
+                        dsf[st][r >> 3][r & 7] = (__bf16)(p * (dp[st][r] - dlt));
                     }
-                    dsf[st][r >> 3][r & 7] = (__bf16)(p * (dp[st][r] - dlt));
-                }
-            // dQ^T += K^T dS^T, K^T by transpose reads of the K tile.
+            };
+            if ((CAUSAL && kb * kBc + kBc - 1 > qw0) || kb * kBc + kBc > N)
+                make_ds(std::true_type{});
+            else
+                make_ds(std::false_type{});
+            // dQ^T += K^T dS^T, K^T by transpose reads of the K tile (two per MFMA).
 #pragma unroll
             for (int tt = 0; tt < D / 32; ++tt)
 #pragma unroll
@@ -472,14 +493,21 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const int base = (st * 32 + h2 * 16) * TL::kRowBytes;
                         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(kt + base + t_off[tt][0]));
+                            (lds_s16x4*)(kt + base + (t_base[0] ^ (tt << 6))));
                         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(kt + base + t_off[tt][1]));
+                            (lds_s16x4*)(kt + base + (t_base[1] ^ (tt << 6))));
                         const s16x4 pair[2] = {lo, hi};
                         bf16x8 ka;
                         __builtin_memcpy(&ka, pair, sizeof(ka));
                         acc[tt] = mfma(ka, dsf[st][h2], acc[tt]);
                     }
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kDqReadAhead, 0);
+#pragma unroll
+            for (int i = 0; i < D / 32 * kBc / 16 - kDqReadAhead; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kDqReadAhead, 0);
         }
         if (kb + 1 < nkb) {
             __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
