@@ -1,0 +1,60 @@
+"""The committed profile summaries match the kernel sources they describe (CPU only).
+
+`bench.py` fills `roofline.traffic` from `profiles/hbm_traffic_*.json` only when
+that file's kernel-source digest equals the digest of the sources as they are
+now; these tests catch a kernel edit that was not followed by new counters and
+a new summary.
+"""
+import importlib.util
+import json
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+
+# pass -> the summary that reports its kernel trace and HBM traffic
+SUMMARIES = {
+    "fwd": ["hbm_traffic_longdoc8k.md", "fa_fwd_bf16_longdoc8k_kernel_trace.md"],
+    "bwd": ["fa_bwd_bf16_longdoc8k.md"],
+    "std": ["fa_std_longdoc8k.md"],
+    "fp8": ["fa_fwd_fp8_longdoc8k.md"],
+    "decode": ["fa_decode_paged_decode50.md"],
+}
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("pass_", sorted(SUMMARIES))
+def test_traffic_counters_match_current_sources(bench, pass_):
+    path = bench.TRAFFIC_FILES[pass_]
+    with open(path) as f:
+        rec = json.load(f)
+    assert rec["pass"] == pass_
+    assert rec["kernel_source_digest"] == bench.kernel_source_digest(pass_), (
+        f"{os.path.basename(path)} was taken on other kernel sources: re-take FETCH_SIZE/WRITE_SIZE")
+    assert rec["hbm_bytes_per_launch"] > 0
+    assert rec["command"], "the counters' command line is recorded"
+
+
+@pytest.mark.parametrize("pass_", sorted(SUMMARIES))
+def test_summaries_name_the_current_digest(bench, pass_):
+    digest = bench.kernel_source_digest(pass_)
+    for name in SUMMARIES[pass_]:
+        with open(os.path.join(PROFILES, name)) as f:
+            text = f.read()
+        assert digest in text, f"{name} does not describe the current sources ({digest})"
+        assert "rocprofv3" in text, f"{name} gives the command that produced it"
+
+
+def test_profiles_hold_text_only():
+    for name in os.listdir(PROFILES):
+        assert os.path.splitext(name)[1] in (".md", ".txt", ".json"), name
+        assert os.path.getsize(os.path.join(PROFILES, name)) < 64 * 1024, name
