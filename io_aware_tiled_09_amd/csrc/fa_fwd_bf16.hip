@@ -35,9 +35,10 @@
 //    key k and lane i receives d column i of the 4 keys.
 //  * K and V tiles (64 keys) go from HBM straight into LDS with
 //    buffer_load_dwordx4 ... lds (no VGPR staging) through two rings of four
-//    tiles each (128 KiB at d = 128, one workgroup per CU). Every phase, each
-//    wave issues its share of one tile (V in even phases, K in odd ones),
-//    which has four phases (two tiles) to land before it is read. Ring slot
+//    tiles each (128 KiB at d = 128, one workgroup per CU). Every phase, the
+//    four waves in their softmax phase load one tile (V in even phases, K in
+//    odd ones), which has four phases (two tiles) to land before it is read;
+//    the waves in their MFMA phase issue no memory instruction. Ring slot
 //    and sub-tile offsets are instruction immediates: the loop is unrolled
 //    by the ring size. Buffer-resource bounds make rows past the sequence
 //    end read as 0.
@@ -123,25 +124,46 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // Last tile with a key visible to some row of this wave.
     const int last = CAUSAL ? min(nkb - 1, (qw0 + 31) / kBc) : nkb - 1;
 
-    // Direct loads: this wave's load `it` of a tile fills LDS bytes
-    // [n*1024, n*1024 + 1024), n = wave*L + it; lane i fills the 16-byte slot
-    // i there, i.e. row n*kRowsPerLoad + i / kChunks, physical chunk
-    // i % kChunks, which holds logical chunk (i % kChunks) ^ swz(row).
-    int ld_off[L];
+    // Direct loads. When a set of W waves fills a tile, load `it` of the
+    // set's wave w fills LDS bytes [n*1024, n*1024 + 1024),
+    // n = w*(kTileLoads/W) + it; lane i fills the 16-byte slot i there, i.e.
+    // row n*kRowsPerLoad + i / kChunks, physical chunk i % kChunks, which
+    // holds logical chunk (i % kChunks) ^ swz(row). The prologue's tiles are
+    // loaded by all eight waves (L loads each); in the phase loop each tile is
+    // loaded by the four waves of the group in its softmax phase (2L loads
+    // each), so that a wave in its MFMA phase issues no memory instruction:
+    // its first score MFMA does not queue behind the workgroup's tile loads
+    // at the start of the phase (measured 3% faster than all eight waves
+    // loading every phase).
+    using TG = Tile<D, kPPWaves / 2>;
+    constexpr int LG = TG::kLoadsPerWave;  // = 2L
+    int ld_off[L], gl_off[LG];
 #pragma unroll
     for (int it = 0; it < L; ++it) ld_off[it] = TL::load_offset(wave, it, lane);
-    // This wave's share of tile t of `src` into `dst`. A tile past the last
-    // one is still issued, with an empty buffer range (nothing is read), so
-    // that every wave issues exactly L loads per phase and the vmcnt
-    // arithmetic of the phase loop holds.
-    auto issue = [&](const __bf16* src, int t, unsigned char* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < LG; ++it) gl_off[it] = TG::load_offset(wave & 3, it, lane);
+    // Buffer resource over tile t of `src`. A tile past the last one gets an
+    // empty range (nothing is read), so that the loads are still issued and
+    // the vmcnt arithmetic of the phase loop holds.
+    auto tile_rsrc = [&](const __bf16* src, int t) __attribute__((always_inline)) {
         const int j0 = t * kBc;
         const bool real = t < nkb;
         const unsigned bytes = real ? (unsigned)min(kBc, N - j0) * TL::kRowBytes : 0u;
-        const i32x4 rs = buffer_rsrc(real ? src + (size_t)j0 * D : src, bytes);
+        return buffer_rsrc(real ? src + (size_t)j0 * D : src, bytes);
+    };
+    // This wave's share of tile t of `src` into `dst`, all eight waves loading.
+    auto issue = [&](const __bf16* src, int t, unsigned char* dst) __attribute__((always_inline)) {
+        const i32x4 rs = tile_rsrc(src, t);
 #pragma unroll
         for (int it = 0; it < L; ++it)
             lds_dma16(rs, ld_off[it], lds_addr(dst + (wave * L + it) * 1024));
+    };
+    // This wave's share of tile t, the four waves of its group loading.
+    auto issue_grp = [&](const __bf16* src, int t, unsigned char* dst) __attribute__((always_inline)) {
+        const i32x4 rs = tile_rsrc(src, t);
+#pragma unroll
+        for (int it = 0; it < LG; ++it)
+            lds_dma16(rs, gl_off[it], lds_addr(dst + ((wave & 3) * LG + it) * 1024));
     };
     // Rows of a partial last V tile past the sequence end must hold finite
     // values (their probabilities are 0, and 0 * NaN would leak); they are
@@ -177,15 +199,17 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 #pragma unroll
         for (int s = 0; s < 2; ++s) v_off[tt][s] = vbase + TL::tr_offset(tt, s, lane);
 
-    // S^T tile of 64 keys from the K tile in ring slot `slot`: K fragment
-    // i = st * (D/16) + c is key row st*32 + li, d slice c*16 + lh*8.
+    // S^T tile of 64 keys from the K tile in ring slot `slot`: MFMA i uses
+    // the K fragment of key row st*32 + li, d slice c*16 + lh*8, with
+    // st = i % 2 and c = i / 2, so consecutive MFMAs alternate between the
+    // two 32-key accumulators (no back-to-back accumulator dependency).
     constexpr int kKFrags = kBc / 32 * D / 16;
     auto scores = [&](int slot, f32x16 (&s)[kBc / 32]) __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < kBc / 32; ++st) s[st] = f32x16{};
 #pragma unroll
         for (int i = 0; i < kKFrags; ++i) {
-            const int st = i / (D / 16), c = i % (D / 16);
+            const int st = i % (kBc / 32), c = i / (kBc / 32);
             const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
                 (size_t)(k_off[c] + slot * TL::kBytes + st * 32 * TL::kRowBytes));
             s[st] = mfma(kf, qf[c], s[st]);
@@ -230,30 +254,39 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // tile j, rescale of the output); B(j) is MFMA work only (scores of tile
     // j+1 from K_{j+1}, then O += P_j V_j), so on every SIMD one wave feeds
     // the matrix core while the other runs the softmax.
-    // Loads: every phase starts with each wave's share of one tile, V_{s/2+2}
-    // in even phases and K_{(s-1)/2+4} in odd ones, into the ring slot of the
-    // tile four back (its last reader, group 1's B, ended two phases
-    // earlier); every phase ends with vmcnt(4L), so the loads of phase s-4
-    // have landed: K_t is first read in phase 2t-1, V_t in phase 2t+1.
+    // Loads: phase s starts with one tile, V_{s/2+2} in even phases and
+    // K_{(s-1)/2+4} in odd ones, loaded by the group whose softmax phase it
+    // is (group s % 2; 2L loads per wave) into the ring slot of the tile four
+    // back (its last reader, group 1's B, ended two phases earlier). A wave
+    // thus issues 2L loads every other phase, and every phase ends with
+    // vmcnt(4L): at the end of phase s the wave's loads of phases s and s-2
+    // may still be in flight, those of phase s-4 have landed, and the
+    // barrier publishes them. K_t is first read in phase 2t-1, V_t in phase
+    // 2t+1.
     auto phase_loads = [&](int s) __attribute__((always_inline)) {
+        if ((s & 1) != grp) return;
         if ((s & 1) == 0) {
             const int t = s / 2 + 2;
-            issue(vh, t, vring[t & 3]);
+            issue_grp(vh, t, vring[t & 3]);
         } else {
             const int t = (s - 1) / 2 + 4;
-            issue(kh, t, kring[t & 3]);
+            issue_grp(kh, t, kring[t & 3]);
         }
     };
     // The partial last V tile, if any, was issued in phase 2*nkb - 6 (when
     // nkb > 2) and has landed at the end of phase 2*nkb - 2, one phase before
-    // it is first read; it is cleared there. The scheduling fences keep every
+    // it is first read; it is cleared there, after a barrier (only the
+    // loading group's waits cover it). The scheduling fences keep every
     // instruction inside its phase: the compiler would otherwise move MFMAs
     // and VALU work across the barrier and break the pairing of the groups.
     const int tail_phase = (nkb > 2 && N % kBc != 0 && nkb == nkb_all) ? 2 * nkb - 2 : -1;
     auto phase_end = [&](int s) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * L));
-        if (s == tail_phase) clear_tail(nkb - 1, vring[(nkb - 1) & 3]);
+        if (s == tail_phase) {
+            __syncthreads();
+            clear_tail(nkb - 1, vring[(nkb - 1) & 3]);
+        }
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -268,13 +301,28 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     auto phase_a = [&](int kb) __attribute__((always_inline)) {
         if (kb > last) return;
         if (kb >= nfull_w) mask(kb, sc);
-        float mr4[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+        // Row max of the lane's 32 scores in four v_max3 chains, then with the
+        // partner lane. The scores are finite or -inf; written as instructions
+        // because fmaxf would add a canonicalizing move per MFMA result.
+        float mr4[4];
 #pragma unroll
-        for (int st = 0; st < kBc / 32; ++st)
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int st = c4 >> 1, r0 = (c4 & 1) * 8;
+            float m = sc[st][r0];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mr4[r & 3] = fmaxf(mr4[r & 3], sc[st][r]);
-        float mraw = fmaxf(fmaxf(mr4[0], mr4[1]), fmaxf(mr4[2], mr4[3]));
-        mraw = max_with_partner(mraw);
+            for (int r = 1; r < 7; r += 2)
+                asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(m), "v"(sc[st][r0 + r]), "v"(sc[st][r0 + r + 1]));
+            asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m), "v"(sc[st][r0 + 7]));
+            mr4[c4] = m;
+        }
+        float mraw;
+        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mraw) : "v"(mr4[0]), "v"(mr4[1]), "v"(mr4[2]));
+        asm("v_max_f32 %0, %1, %2" : "=v"(mraw) : "v"(mraw), "v"(mr4[3]));
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw), __float_as_uint(mraw),
+                                                             false, false);
+            asm("v_max_f32 %0, %1, %2" : "=v"(mraw) : "v"(__uint_as_float(sw[0])), "v"(__uint_as_float(sw[1])));
+        }
         // scale >= 0, so the scaled max is scale_log2 * raw max
         const float mtile = mraw > neg_inf() ? mraw * scale_log2 : neg_inf();
         const bool grow = mtile > m_run;
@@ -312,12 +360,14 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, kReadAhead, 0);
         }
         if (kb > last) return;
+        // 16-key chunk outer, 32-column block inner: consecutive MFMAs update
+        // different accumulators.
 #pragma unroll
-        for (int tt = 0; tt < D / 32; ++tt) {
+        for (int st = 0; st < kBc / 32; ++st)
 #pragma unroll
-            for (int st = 0; st < kBc / 32; ++st)
+            for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
+                for (int tt = 0; tt < D / 32; ++tt) {
                     const unsigned off = vslot * TL::kBytes + (st * 32 + h2 * 16) * TL::kRowBytes;
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (lds_s16x4*)(size_t)(v_off[tt][0] + off));
@@ -328,7 +378,6 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                     __builtin_memcpy(&vf, lohi, sizeof(vf));
                     acc[tt] = mfma(vf, pf[st][h2], acc[tt]);
                 }
-        }
         // V fragments (two transpose reads each) kReadAhead MFMAs ahead.
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kReadAhead, 0);
 #pragma unroll
