@@ -79,15 +79,17 @@ def kernel_source_digest(pass_: str = "fwd") -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(digest: str, pass_: str = "fwd"):
+def measured_traffic(digest: str, pass_: str = "fwd", workload: str = ""):
     """HBM bytes per call from the committed rocprofv3 counter summary, if it
-    was taken on this exact kernel source; else None."""
+    was taken on this exact kernel source and workload; else None."""
     try:
         with open(TRAFFIC_FILES[pass_]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_digest") != digest:
+        return None
+    if workload and t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -155,6 +157,33 @@ def ingest_counters(fetch_csv, write_csv, copy_mib, command, pass_="fwd"):
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
     return 0
+
+
+def gemm_reference(torch, stream, achieved_tflops, n=8192, iters=10):
+    """Same-box reference for the MFMA rate: torch's bf16 GEMM (hipBLASLt) at
+    n^3, timed with HIP events on the bench stream after the timed region. The
+    2.5 PFLOP/s datasheet peak assumes a 2.4 GHz engine clock that dense MFMA
+    work does not hold on these boards; this number says what a vendor GEMM
+    reaches on the same GPU in the same run."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            c = a @ b
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            c = a @ b
+        e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    log(f"reference bf16 GEMM {n}^3: {ms:.4f} ms -> {tflops:.1f} TFLOP/s")
+    return {"what": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), same GPU and run",
+            "tflops": round(tflops, 1), "ms": round(ms, 4),
+            "kernel_over_reference": round(achieved_tflops / tflops, 4)}
 
 
 def cpu_baseline(w, q, k, v, budget_s: float, fp8=None):
@@ -298,7 +327,7 @@ def bench_decode(args):
                    "algorithmic_bytes": nbytes, "pass": "decode"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(digest, "decode"),
+                     "traffic": measured_traffic(digest, "decode", name),
                      "avg_launch_ms": round(avg_ms, 5),
                      "kernels": list(PASS_KERNELS["decode"]), "kernel_source_digest": digest},
         "cpu_baseline": None,
@@ -334,6 +363,10 @@ def main(argv=None):
                          "decode50 by default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--gemm-ref", type=int, default=1,
+                    help="after the timed region, time torch's bf16 GEMM (8192^3, hipBLASLt) "
+                         "on the same stream as a same-box reference of the MFMA rate the "
+                         "chip sustains (0 = skip; bf16 fwd/bwd passes only)")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB 3 times "
                          "(reference kernel for HBM counter calibration)")
@@ -490,7 +523,7 @@ def main(argv=None):
         log(f"copy kernel: {args.copy_kernel_mib} MiB read + written, 3 times")
 
     digest = kernel_source_digest(args.pass_)
-    traffic = measured_traffic(digest, args.pass_)
+    traffic = measured_traffic(digest, args.pass_, w.name)
     metric = "attention fwd TFLOP/s (bf16, 1 MI355X) at N=8K d=128 causal; % of MFMA peak"
     if bwd:
         metric = ("attention bwd TFLOP/s (bf16, 1 MI355X) at N=8K d=128 causal; % of MFMA peak "
@@ -551,6 +584,8 @@ def main(argv=None):
             "kernel_source_digest": digest,
             "call_ms": round(avg_launch_ms, 5),
         }
+    if args.gemm_ref and not (fp8 or stdp):
+        result["mfma_reference"] = gemm_reference(torch, stream, achieved)
     if args.cpu_budget > 0:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do_cpu, args.cpu_budget) if bwd
