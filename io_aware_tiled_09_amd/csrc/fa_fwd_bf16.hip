@@ -87,7 +87,7 @@ constexpr int kReadAhead = 6;
 constexpr float kMaxSlack = 3.0f;
 static_assert(kBrBf16 == kPPWaves * 32, "32 query rows per wave");
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAIRED>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                         const __bf16* __restrict__ v, __bf16* __restrict__ o,
@@ -107,8 +107,22 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     const int li = lane & 31;   // query column of this lane in the wave's 32
     const int lh = lane >> 5;   // which 8-element half of each 16-wide k slice
 
-    int qb, bh;
-    block_coords<CAUSAL>(blockIdx.x, BH, nqb, qb, bh);
+    // Work items: one query block per workgroup, or (PAIRED, causal) the two
+    // blocks nqb-1-p and p of a head one after the other, so that every
+    // workgroup has the same number of key tiles.
+    int first, second, nitems, bh;
+    if constexpr (PAIRED) {
+        block_coords<CAUSAL>(blockIdx.x, BH, (nqb + 1) / 2, second, bh);
+        first = nqb - 1 - second;
+        nitems = first == second ? 1 : 2;
+    } else {
+        block_coords<CAUSAL>(blockIdx.x, BH, nqb, first, bh);
+        second = first;
+        nitems = 1;
+    }
+    for (int item = 0; item < nitems; ++item) {
+    const int qb = item == 0 ? first : second;
+    if (item) __syncthreads();  // the previous block's LDS reads are done
     const size_t head_off = (size_t)bh * (size_t)N * D;
     const __bf16* qh = q + head_off;
     const __bf16* kh = k + head_off;
@@ -449,16 +463,37 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         if (lh == 0)
             lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
     }
+    }  // work items
 }
+
+// Causal grids of at most two workgroups per CU run one workgroup per pair
+// of query blocks: with one block each, the heavy blocks (many key tiles)
+// and the light ones land unevenly on the CUs. For d = 64 up to N = 8192
+// the pairing also pays on larger grids (two heads' K and V, 2 x 2 MiB at
+// N = 8192, still fit an XCD's 4 MB L2); for d = 128 on larger grids it
+// costs 8-20% (measured), so those keep one block per workgroup.
+constexpr long long kPairMaxGrid = 2 * 256;  // 256 CUs on MI355X
 
 template <int D, bool CAUSAL>
 hipError_t launch_one(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
                       int BH, int N, float scale_log2, hipStream_t stream)
 {
     const int nqb = (N + kBrBf16 - 1) / kBrBf16;
-    const dim3 grid((unsigned)((long long)BH * nqb));
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kPPThreads), 0, stream, q, k,
-                       v, o, lse, BH, N, nqb, scale_log2);
+    const long long blocks = (long long)BH * nqb;
+    const bool paired = nqb > 1 && (blocks <= kPairMaxGrid || (D == 64 && N <= 8192));
+    if constexpr (CAUSAL) {
+        if (paired) {
+            const dim3 grid((unsigned)((long long)BH * ((nqb + 1) / 2)));
+            hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, true, true>), grid, dim3(kPPThreads), 0,
+                               stream, q, k, v, o, lse, BH, N, nqb, scale_log2);
+            return hipGetLastError();
+        }
+    }
+    {
+        const dim3 grid((unsigned)blocks);
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, false>), grid, dim3(kPPThreads), 0, stream,
+                           q, k, v, o, lse, BH, N, nqb, scale_log2);
+    }
     return hipGetLastError();
 }
 

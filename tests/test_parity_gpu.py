@@ -39,6 +39,17 @@ def test_ragged_multi_tile(d, causal):
     check_full(q, k, v, causal, 1.0 / math.sqrt(d), "N=333")
 
 
+@pytest.mark.parametrize("B,H,N,d", [(1, 3, 700, 64), (1, 3, 700, 128), (2, 2, 1300, 128),
+                                     (1, 2, 2100, 64), (3, 1, 513, 128)])
+def test_paired_query_blocks(B, H, N, d):
+    # Causal grids this small run one workgroup per pair of query blocks
+    # (nqb-1-p, p); odd block counts leave the middle block alone and ragged
+    # N puts the partial block in a pair.
+    say(f"paired blocks B={B} H={H} N={N} d={d} causal")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=N + d + B)
+    check_full(q, k, v, True, 1.0 / math.sqrt(d), f"paired N={N} d={d}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp32_storage_path(d):
     say(f"fp32 storage B=2 H=2 N=300 d={d}")
