@@ -336,11 +336,14 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         // buffers and P(t - 1) are no longer read.
         __syncthreads();
         float next_stats = 0.f;
+        if (!pwave) dscores(t);
+        // Tile t+2's loads after dS(t), so that the P-wave's first dV MFMAs
+        // and the dS-wave's VALU work do not queue behind them (1% faster
+        // than issuing them at the start of the step).
         if (t + 2 < nqt) {
             load_tile(t + 2);
             next_stats = fetch_stats(t + 2);
         }
-        if (!pwave) dscores(t);
         accumulate(t);
         if (t + 1 < nqt) {
             scores(t + 1);
