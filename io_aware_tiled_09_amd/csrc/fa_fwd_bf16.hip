@@ -145,9 +145,6 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 
     const int nkb_all = (N + kBc - 1) / kBc;
     const int nkb = CAUSAL ? min(nkb_all, (q0 + kBrBf16 - 1) / kBc + 1) : nkb_all;
-    // Tiles [0, nfull) need no mask for any wave of the workgroup: all their
-    // keys are < N and (causal) <= the workgroup's first query q0.
-    const int nfull = min(CAUSAL ? (q0 + 1) / kBc : nkb_all, N / kBc);
     // Last tile with a key visible to some row of this wave.
     const int last = CAUSAL ? min(nkb - 1, (qw0 + 31) / kBc) : nkb - 1;
 
