@@ -186,6 +186,31 @@ def gemm_reference(torch, stream, achieved_tflops, n=8192, iters=10):
             "kernel_over_reference": round(achieved_tflops / tflops, 4)}
 
 
+def hbm_reference(torch, stream, achieved_gbs, mib=1024, iters=10):
+    """Same-box reference for the HBM rate: torch's device copy of `mib` MiB
+    (bytes read + written), timed with HIP events on the bench stream after
+    the timed region."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            dst.copy_(src)
+        e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    gbs = 2.0 * n * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    log(f"reference device copy {mib} MiB: {ms:.4f} ms -> {gbs:.0f} GB/s")
+    return {"what": f"torch device copy of {mib} MiB (read + write), same GPU and run",
+            "gbs": round(gbs, 1), "ms": round(ms, 4),
+            "kernel_over_reference": round(achieved_gbs / gbs, 4)}
+
+
 def cpu_baseline(w, q, k, v, budget_s: float, fp8=None):
     """Time the oracle over whole heads of the workload until about budget_s.
     fp8: ((q8, k8, v8), (q_scale, k_scale, v_scale)) to time the oracle on the
@@ -332,6 +357,8 @@ def bench_decode(args):
                      "kernels": list(PASS_KERNELS["decode"]), "kernel_source_digest": digest},
         "cpu_baseline": None,
     }
+    if args.gemm_ref:
+        result["hbm_reference"] = hbm_reference(torch, torch.cuda.current_stream(), achieved)
     if args.cpu_budget > 0:
         import oracle
         t0 = time.perf_counter()
@@ -364,9 +391,10 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--gemm-ref", type=int, default=1,
-                    help="after the timed region, time torch's bf16 GEMM (8192^3, hipBLASLt) "
-                         "on the same stream as a same-box reference of the MFMA rate the "
-                         "chip sustains (0 = skip; bf16 fwd/bwd passes only)")
+                    help="after the timed region, time a same-box reference on the same "
+                         "stream: torch's bf16 GEMM (8192^3, hipBLASLt) for the bf16 fwd/bwd "
+                         "passes (MFMA rate the chip sustains), torch's 1 GiB device copy for "
+                         "the std and decode passes (HBM rate); 0 = skip")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB 3 times "
                          "(reference kernel for HBM counter calibration)")
@@ -589,6 +617,8 @@ def main(argv=None):
         }
     if args.gemm_ref and not (fp8 or stdp):
         result["mfma_reference"] = gemm_reference(torch, stream, achieved)
+    if args.gemm_ref and stdp:
+        result["hbm_reference"] = hbm_reference(torch, stream, sm_gbs)
     if args.cpu_budget > 0:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do_cpu, args.cpu_budget) if bwd
