@@ -58,3 +58,20 @@ def test_profiles_hold_text_only():
     for name in os.listdir(PROFILES):
         assert os.path.splitext(name)[1] in (".md", ".txt", ".json"), name
         assert os.path.getsize(os.path.join(PROFILES, name)) < 64 * 1024, name
+
+
+@pytest.mark.parametrize("pass_", sorted(SUMMARIES))
+def test_traffic_is_reported_only_for_its_workload(bench, pass_):
+    # roofline.traffic comes from a counter run on one workload; another
+    # workload (or another kernel source) reports null instead.
+    with open(bench.TRAFFIC_FILES[pass_]) as f:
+        rec = json.load(f)
+    digest = bench.kernel_source_digest(pass_)
+    assert bench.measured_traffic(digest, pass_, rec["workload"]) == rec["hbm_bytes_per_launch"]
+    assert bench.measured_traffic(digest, pass_, rec["workload"] + "_other") is None
+    assert bench.measured_traffic("0" * 16, pass_, rec["workload"]) is None
+
+
+def test_bench_refuses_more_than_one_gpu(bench, capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
