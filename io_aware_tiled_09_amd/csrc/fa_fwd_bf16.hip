@@ -355,7 +355,24 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         bf16x8 p1[1][kBc / 32][2];
-        const float lsum = probs<false, 1>(sc, scale_log2, m_run, p1);
+        // p = exp2(s c - m) in bf16 for P V, its fp32 sum in four partial
+        // chains that start at -0 (so the first add folds away)
+        float lsum;
+        {
+            float ls[4] = {-0.f, -0.f, -0.f, -0.f};
+#pragma unroll
+            for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const float p = __builtin_amdgcn_exp2f(
+                            __builtin_fmaf(sc[st][h2 * 8 + r], scale_log2, -m_run));
+                        ls[r & 3] += p;
+                        p1[0][st][h2][r] = (__bf16)p;
+                    }
+            lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        }
         l_run = l_run * alpha + lsum;
 #pragma unroll
         for (int st = 0; st < kBc / 32; ++st) {
@@ -438,15 +455,8 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         step(std::integral_constant<int, 2>{}, kb + 2);
         step(std::integral_constant<int, 3>{}, kb + 3);
     }
-    if (grp == 0) {  // group 0's idle last phase
-        const int s_end = 2 * ((nkb + 3) & ~3);
-        phase_loads(s_end);
-        phase_end(s_end);
-    }
-    // No load may still be landing in LDS when the workgroup ends.
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-
     // ---- epilogue: O = acc / l, lse = (m2 + log2 l) * ln 2
+    auto epilogue = [&]() __attribute__((always_inline)) {
     const float l_tot = sum_with_partner(l_run);
     if (qi < N) {
         const float inv = 1.0f / l_tot;
@@ -460,6 +470,18 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         if (lh == 0)
             lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
     }
+    };
+    // Group 0's outputs are final after its last MFMA phase: it stores them in
+    // the phase in which group 1 runs its last MFMA phase (no tile is loaded
+    // or read by group 0 there any more), then meets that phase's barrier.
+    if (grp == 0) {
+        epilogue();
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    }
+    // No load may still be landing in LDS when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    if (grp == 1) epilogue();
     }  // work items
 }
 
