@@ -50,6 +50,25 @@ def test_paired_query_blocks(B, H, N, d):
     check_full(q, k, v, True, 1.0 / math.sqrt(d), f"paired N={N} d={d}")
 
 
+def _random_shapes(n=12, seed=4242):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        out.append((rng.randint(1, 3), rng.randint(1, 3), rng.randint(1, 2600),
+                    rng.choice([64, 128]), rng.choice([False, True])))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", _random_shapes())
+def test_random_shapes(B, H, N, d, causal):
+    # Seeded shapes: query-block counts odd and even, ragged tails, paired and
+    # unpaired grids.
+    say(f"random B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=B * 1000 + H * 100 + N + d)
+    check_full(q, k, v, causal, 1.0 / math.sqrt(d), f"random N={N} d={d}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp32_storage_path(d):
     say(f"fp32 storage B=2 H=2 N=300 d={d}")
