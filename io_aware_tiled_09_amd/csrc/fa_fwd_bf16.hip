@@ -185,9 +185,17 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // This wave's share of tile t, the four waves of its group loading.
     auto issue_grp = [&](const __bf16* src, int t, unsigned char* dst) __attribute__((always_inline)) {
         const i32x4 rs = tile_rsrc(src, t);
+        if constexpr (PAIRED) {
+            // LDS base of this wave's share, formed at the issue (not kept live)
+            unsigned lb = lds_addr(dst + (wave & 3) * LG * 1024);
+            asm volatile("" : "+s"(lb));
 #pragma unroll
-        for (int it = 0; it < LG; ++it)
-            lds_dma16(rs, gl_off[it], lds_addr(dst + ((wave & 3) * LG + it) * 1024));
+            for (int it = 0; it < LG; ++it) lds_dma16(rs, gl_off[it], lb + it * 1024);
+        } else {
+#pragma unroll
+            for (int it = 0; it < LG; ++it)
+                lds_dma16(rs, gl_off[it], lds_addr(dst + ((wave & 3) * LG + it) * 1024));
+        }
     };
     // Rows of a partial last V tile past the sequence end must hold finite
     // values (their probabilities are 0, and 0 * NaN would leak); they are
@@ -210,18 +218,31 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     asm volatile("" : "+s"(kbase), "+s"(vbase));
 
     // K fragment (A operand of S^T): key row st*32 + li, logical chunk 2c + lh.
-    unsigned k_off[D / 16];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) k_off[c] = kbase + TL::frag_offset(li, 2 * c + lh);
-
     // V^T fragment (A operand of O^T += V^T P^T) by two transpose reads: for
     // read s (slots 4s..4s+3) lane l points at key 4*lh + (l % 16) / 4 + 8s of
     // the 16-key chunk and d = tt*32 + ((l / 16) % 2) * 16 + 4 * (l % 4).
+    unsigned k_off[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) k_off[c] = kbase + TL::frag_offset(li, 2 * c + lh);
     unsigned v_off[D / 32][2];
 #pragma unroll
     for (int tt = 0; tt < D / 32; ++tt)
 #pragma unroll
         for (int s = 0; s < 2; ++s) v_off[tt][s] = vbase + TL::tr_offset(tt, s, lane);
+    // The swizzle permutes 16-byte chunks by XOR and the ring bases are
+    // 1024-aligned, so the offsets of chunk c and column block tt differ from
+    // those of c = 0 and tt = 0 only by XOR: k(c) = k(0) ^ (c << 5),
+    // v(tt, s) = v(0, s) ^ (tt << 6). The paired kernel, whose work-item loop
+    // holds more registers, keeps only the three bases live and rebuilds the
+    // rest in every phase; the one-block kernel keeps all offsets.
+    auto k_frag = [&](int c) __attribute__((always_inline)) {
+        if constexpr (PAIRED) return k_off[0] ^ ((unsigned)c << 5);
+        else return k_off[c];
+    };
+    auto v_frag = [&](int tt, int s) __attribute__((always_inline)) {
+        if constexpr (PAIRED) return v_off[0][s] ^ ((unsigned)tt << 6);
+        else return v_off[tt][s];
+    };
 
     // S^T tile of 64 keys from the K tile in ring slot `slot`: MFMA i uses
     // the K fragment of key row st*32 + li, d slice c*16 + lh*8, with
@@ -235,7 +256,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         for (int i = 0; i < kKFrags; ++i) {
             const int st = i % (kBc / 32), c = i / (kBc / 32);
             const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-                (size_t)(k_off[c] + slot * TL::kBytes + st * 32 * TL::kRowBytes));
+                (size_t)(k_frag(c) + slot * TL::kBytes + st * 32 * TL::kRowBytes));
             s[st] = mfma(kf, qf[c], s[st]);
         }
     };
@@ -390,6 +411,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // B(j): MFMA work only. Scores of tile j+1 from K ring slot kslot, then
     // O^T += V_j^T P_j^T from V ring slot vslot.
     auto phase_b = [&](int kb, int kslot, int vslot) __attribute__((always_inline)) {
+        if constexpr (PAIRED) asm volatile("" : "+v"(k_off[0]), "+v"(v_off[0][0]), "+v"(v_off[0][1]));
         if (kb + 1 <= last) {
             scores(kslot, sc);
             // K fragments kReadAhead MFMAs ahead, no further (VGPR budget).
@@ -412,9 +434,9 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                 for (int tt = 0; tt < D / 32; ++tt) {
                     const unsigned off = vslot * TL::kBytes + (st * 32 + h2 * 16) * TL::kRowBytes;
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(size_t)(v_off[tt][0] + off));
+                        (lds_s16x4*)(size_t)(v_frag(tt, 0) + off));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(size_t)(v_off[tt][1] + off));
+                        (lds_s16x4*)(size_t)(v_frag(tt, 1) + off));
                     const s16x4 lohi[2] = {lo, hi};
                     bf16x8 vf;
                     __builtin_memcpy(&vf, lohi, sizeof(vf));
@@ -485,13 +507,14 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     }  // work items
 }
 
-// Causal grids of at most two workgroups per CU run one workgroup per pair
-// of query blocks: with one block each, the heavy blocks (many key tiles)
-// and the light ones land unevenly on the CUs. For d = 64 up to N = 8192
-// the pairing also pays on larger grids (two heads' K and V, 2 x 2 MiB at
-// N = 8192, still fit an XCD's 4 MB L2); for d = 128 on larger grids it
-// costs 8-20% (measured), so those keep one block per workgroup.
+// Causal grids run one workgroup per pair of query blocks (the i-th
+// heaviest with the i-th lightest) when the grid is small or N <= 8192: with
+// one block each, the heavy blocks (many key tiles) and the light ones land
+// unevenly on the CUs. The paired kernel measured 1-17% faster for d = 128
+// causal at N <= 8192 on grids of 1024-2048 blocks, and even at N = 16384,
+// so longer sequences keep one block per workgroup.
 constexpr long long kPairMaxGrid = 2 * 256;  // 256 CUs on MI355X
+constexpr int kPairMaxN = 8192;
 
 template <int D, bool CAUSAL>
 hipError_t launch_one(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
@@ -499,7 +522,7 @@ hipError_t launch_one(const __bf16* q, const __bf16* k, const __bf16* v, __bf16*
 {
     const int nqb = (N + kBrBf16 - 1) / kBrBf16;
     const long long blocks = (long long)BH * nqb;
-    const bool paired = nqb > 1 && (blocks <= kPairMaxGrid || (D == 64 && N <= 8192));
+    const bool paired = nqb > 1 && (blocks <= kPairMaxGrid || N <= kPairMaxN);
     if constexpr (CAUSAL) {
         if (paired) {
             const dim3 grid((unsigned)((long long)BH * ((nqb + 1) / 2)));

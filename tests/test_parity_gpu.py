@@ -42,12 +42,26 @@ def test_ragged_multi_tile(d, causal):
 @pytest.mark.parametrize("B,H,N,d", [(1, 3, 700, 64), (1, 3, 700, 128), (2, 2, 1300, 128),
                                      (1, 2, 2100, 64), (3, 1, 513, 128)])
 def test_paired_query_blocks(B, H, N, d):
-    # Causal grids this small run one workgroup per pair of query blocks
+    # Causal grids with N <= 8192 run one workgroup per pair of query blocks
     # (nqb-1-p, p); odd block counts leave the middle block alone and ragged
     # N puts the partial block in a pair.
     say(f"paired blocks B={B} H={H} N={N} d={d} causal")
     q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=N + d + B)
     check_full(q, k, v, True, 1.0 / math.sqrt(d), f"paired N={N} d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_unpaired_causal_ragged(d):
+    # Past N = 8192 a causal grid of more than 512 query blocks runs one block
+    # per workgroup; N = 8300 leaves a ragged last block of 108 rows.
+    B, H, N = 1, 16, 8300
+    say(f"unpaired causal B={B} H={H} N={N} d={d}")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=8300 + d)
+    rows = sample_rows(N, 24, seed=91 + d, heads=B * H)
+    fixed = torch.tensor([0, 255, 256, 4095, 8191, 8192, 8255, 8256, N - 2, N - 1],
+                         dtype=torch.int64)
+    check_rows(q, k, v, True, 1.0 / math.sqrt(d), torch.cat([rows, fixed.expand(B * H, -1)], 1),
+               f"unpaired N={N} d={d}")
 
 
 def _random_shapes(n=12, seed=4242):
