@@ -64,6 +64,20 @@ def test_unpaired_causal_ragged(d):
                f"unpaired N={N} d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_paired_long_ragged(d):
+    # N = 8000 <= 8192: the paired kernel over 32 query blocks (16 pairs) per
+    # head, the last block ragged (64 rows) and paired with block 0.
+    B, H, N = 1, 4, 8000
+    say(f"paired long ragged B={B} H={H} N={N} d={d}")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=8000 + d)
+    rows = sample_rows(N, 32, seed=57 + d, heads=B * H)
+    fixed = torch.tensor([0, 1, 255, 256, 3967, 3968, 4031, 7935, 7936, 7937, N - 2, N - 1],
+                         dtype=torch.int64)
+    check_rows(q, k, v, True, 1.0 / math.sqrt(d), torch.cat([rows, fixed.expand(B * H, -1)], 1),
+               f"paired long N={N} d={d}")
+
+
 def _random_shapes(n=12, seed=4242):
     import random
     rng = random.Random(seed)
