@@ -85,19 +85,77 @@ int oracle_softmax_row(const double *s, const double *v, long n, long dv,
 }
 
 /*
- * Online softmax, block-local form with two correction factors, for one row.
+ * Partial softmax state of one row over a subset of its keys:
+ *   m   = the largest score in the subset (the exponent offset),
+ *   l   = sum over the subset of exp(s_j - m),
+ *   acc = sum over the subset of exp(s_j - m) * v_j   (dv values).
+ * The empty subset (or one whose scores are all -inf) is m = -inf, l = 0,
+ * acc = 0. Two states of disjoint subsets combine into the state of their
+ * union by moving both to the common offset max(m_a, m_b); the combination
+ * is associative and commutative, so any blocking of a row gives the same
+ * state up to rounding.
+ * [P2, "The fix: tile the computation, never materialize the full matrix":
+ *  the per-block max, sum and weighted sum, and the combination of a running
+ *  result with a new block through two correction factors]
+ */
+typedef struct {
+    double m;
+    double l;
+    double *acc;
+} row_state;
+
+/* State of keys [lo, hi) of a row, computed from its own max. */
+static void state_of_keys(const double *s, const double *v, long lo, long hi,
+                          long dv, row_state *st)
+{
+    st->m = -INFINITY;
+    for (long j = lo; j < hi; ++j)
+        st->m = s[j] > st->m ? s[j] : st->m;
+    st->l = 0.0;
+    for (long t = 0; t < dv; ++t)
+        st->acc[t] = 0.0;
+    if (!(st->m > -INFINITY))
+        return; /* every key of the subset masked: the empty state */
+    for (long j = lo; j < hi; ++j) {
+        const double w = exp(s[j] - st->m);
+        st->l += w;
+        for (long t = 0; t < dv; ++t)
+            st->acc[t] += w * v[j * dv + t];
+    }
+}
+
+/* *a becomes the state of the union of a's and b's (disjoint) subsets. */
+static void state_combine(row_state *a, const row_state *b, long dv)
+{
+    if (!(b->l > 0.0))
+        return; /* b is empty */
+    if (!(a->l > 0.0)) {
+        a->m = b->m;
+        a->l = b->l;
+        for (long t = 0; t < dv; ++t)
+            a->acc[t] = b->acc[t];
+        return;
+    }
+    const double offset = a->m > b->m ? a->m : b->m;
+    const double fa = exp(a->m - offset), fb = exp(b->m - offset);
+    a->l = a->l * fa + b->l * fb;
+    for (long t = 0; t < dv; ++t)
+        a->acc[t] = a->acc[t] * fa + b->acc[t] * fb;
+    a->m = offset;
+}
+
+/*
+ * Online softmax of one row in block-local form: the row is cut into blocks
+ * of `block` consecutive keys, each block's state is computed on its own
+ * (state_of_keys) and combined into the running state (state_combine) in
+ * key order; the output is acc / l of the final state.
  * [P2, "The fix: tile the computation, never materialize the full matrix"]
  * [P2, "Tracing the algorithm as code"]
  *
- * For every block of `block` consecutive scores: local max, exponentials
- * relative to it, local sum and local weighted sum; then merge into the
- * running (m, l, acc) with exp(m_old - m_new) and exp(m_block - m_new).
- * Before the first block m = -inf, l = 0, acc = 0, so exp(m_old - m_new) is
- * exactly 0 there. Output is acc / l.
- *
  * Reading for a case the pages do not cover: a block whose scores are all
- * -inf (all masked) contributes nothing, instead of producing exp(-inf+inf).
- * m_out / l_out (may be NULL) receive the final running max and sum.
+ * -inf (all masked) is the empty state and changes nothing, instead of
+ * producing exp(-inf + inf).
+ * m_out / l_out (may be NULL) receive the final state's offset and sum.
  */
 int oracle_online_row_two_scale(const double *s, const double *v, long n,
                                 long dv, long block, double *out,
@@ -105,51 +163,30 @@ int oracle_online_row_two_scale(const double *s, const double *v, long n,
 {
     if (!s || !v || !out || n < 1 || dv < 1 || block < 1)
         return ORACLE_ERR_ARG;
-    double *acc = (double *)calloc((size_t)dv, sizeof(double));
-    double *acc_blk = (double *)malloc((size_t)dv * sizeof(double));
-    if (!acc || !acc_blk) {
-        free(acc);
-        free(acc_blk);
+    row_state run = {-INFINITY, 0.0, (double *)calloc((size_t)dv, sizeof(double))};
+    row_state part = {-INFINITY, 0.0, (double *)calloc((size_t)dv, sizeof(double))};
+    if (!run.acc || !part.acc) {
+        free(run.acc);
+        free(part.acc);
         return ORACLE_ERR_NOMEM;
     }
-    double m = -INFINITY, l = 0.0;
-    for (long start = 0; start < n; start += block) {
-        long end = start + block < n ? start + block : n;
-        double m_blk = -INFINITY;
-        for (long j = start; j < end; ++j)
-            if (s[j] > m_blk)
-                m_blk = s[j];
-        if (!(m_blk > -INFINITY))
-            continue; /* fully masked block */
-        double l_blk = 0.0;
-        for (long t = 0; t < dv; ++t)
-            acc_blk[t] = 0.0;
-        for (long j = start; j < end; ++j) {
-            double p = exp(s[j] - m_blk);
-            l_blk += p;
-            for (long t = 0; t < dv; ++t)
-                acc_blk[t] += p * v[j * dv + t];
-        }
-        double m_new = m > m_blk ? m : m_blk;
-        double scale_old = exp(m - m_new);
-        double scale_new = exp(m_blk - m_new);
-        l = l * scale_old + l_blk * scale_new;
-        for (long t = 0; t < dv; ++t)
-            acc[t] = acc[t] * scale_old + acc_blk[t] * scale_new;
-        m = m_new;
+    for (long lo = 0; lo < n; lo += block) {
+        const long hi = lo + block < n ? lo + block : n;
+        state_of_keys(s, v, lo, hi, dv, &part);
+        state_combine(&run, &part, dv);
     }
     int rc = ORACLE_OK;
-    if (!(l > 0.0))
+    if (!(run.l > 0.0))
         rc = ORACLE_ERR_ARG; /* every score was -inf */
     else
         for (long t = 0; t < dv; ++t)
-            out[t] = acc[t] / l;
+            out[t] = run.acc[t] / run.l;
     if (m_out)
-        *m_out = m;
+        *m_out = run.m;
     if (l_out)
-        *l_out = l;
-    free(acc);
-    free(acc_blk);
+        *l_out = run.l;
+    free(run.acc);
+    free(part.acc);
     return rc;
 }
 
@@ -429,27 +466,58 @@ int oracle_attention_bwd(const double *q, const double *k, const double *v,
                 dSi[j] = Pi[j] * (dSi[j] - Di);
             D[i] = Di;
         }
-        /* dQ = scale dS K (rows i) */
-#pragma omp parallel for schedule(static)
-        for (long i = 0; i < N; ++i)
-            for (long t = 0; t < d; ++t) {
-                double acc = 0.0;
-                for (long j = 0; j < N; ++j)
-                    acc += dS[(size_t)i * N + j] * kh[j * d + t];
-                dqh[i * d + t] = scale * acc;
-            }
-        /* dK = scale dS^T Q and dV = P^T dO (rows j) */
-#pragma omp parallel for schedule(static)
-        for (long j = 0; j < N; ++j)
-            for (long t = 0; t < d; ++t) {
-                double ak = 0.0, av = 0.0;
-                for (long i = 0; i < N; ++i) {
-                    ak += dS[(size_t)i * N + j] * qh[i * d + t];
-                    av += P[(size_t)i * N + j] * doh[i * d + t];
+        /* dQ = scale dS K (rows i). Each dQ_it is the sum over j = 0..N-1 in
+         * ascending order; the t loop is innermost so that K is read by rows. */
+#pragma omp parallel
+        {
+            double *acc = (double *)malloc((size_t)d * sizeof(double));
+#pragma omp for schedule(static)
+            for (long i = 0; i < N; ++i) {
+                for (long t = 0; t < d; ++t)
+                    acc[t] = 0.0;
+                for (long j = 0; j < N; ++j) {
+                    const double w = dS[(size_t)i * N + j];
+                    for (long t = 0; t < d; ++t)
+                        acc[t] += w * kh[j * d + t];
                 }
-                dkh[j * d + t] = scale * ak;
-                dvh[j * d + t] = av;
+                for (long t = 0; t < d; ++t)
+                    dqh[i * d + t] = scale * acc[t];
             }
+            free(acc);
+        }
+        /* dK = scale dS^T Q and dV = P^T dO (rows j), for a run of kKeyRun key
+         * rows at a time. Each dK_jt and dV_jt is the sum over i = 0..N-1 in
+         * ascending order, as in the plain column-by-column loop; the i loop
+         * is outermost so that dS and P are read by rows. */
+        enum { kKeyRun = 32 };
+#pragma omp parallel
+        {
+            double *ak = (double *)malloc((size_t)kKeyRun * (size_t)d * sizeof(double));
+            double *av = (double *)malloc((size_t)kKeyRun * (size_t)d * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+            for (long j0 = 0; j0 < N; j0 += kKeyRun) {
+                const long nj = j0 + kKeyRun < N ? kKeyRun : N - j0;
+                for (long x = 0; x < nj * d; ++x)
+                    ak[x] = av[x] = 0.0;
+                for (long i = 0; i < N; ++i) {
+                    const double *dSi = dS + (size_t)i * N + j0, *Pi = P + (size_t)i * N + j0;
+                    for (long jj = 0; jj < nj; ++jj) {
+                        const double ws = dSi[jj], wp = Pi[jj];
+                        for (long t = 0; t < d; ++t) {
+                            ak[jj * d + t] += ws * qh[i * d + t];
+                            av[jj * d + t] += wp * doh[i * d + t];
+                        }
+                    }
+                }
+                for (long jj = 0; jj < nj; ++jj)
+                    for (long t = 0; t < d; ++t) {
+                        dkh[(j0 + jj) * d + t] = scale * ak[jj * d + t];
+                        dvh[(j0 + jj) * d + t] = av[jj * d + t];
+                    }
+            }
+            free(ak);
+            free(av);
+        }
         if (delta)
             memcpy(delta + (size_t)bh * (size_t)N, D, (size_t)N * sizeof(double));
     }
