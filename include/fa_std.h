@@ -7,7 +7,7 @@
  * product with V; these round trips, not the arithmetic, dominate its time.
  * [FlashAttention: The GPU Memory Hack That Changed Everything
  *  (ai.branddocks.com, episode 75), "Standard Attention" and "The Problem:
- *  Memory Bandwidth"]
+ *  GPU Memory Hierarchy"]
  * [Flash Attention Optimization (aicomputerinstitute.com), "Attention is not
  *  slow because of arithmetic"]
  *

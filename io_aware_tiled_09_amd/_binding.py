@@ -142,6 +142,33 @@ def fa_tile_cols() -> int:
     return int(load().fa_tile_cols())
 
 
+def _need(t, name, shape, dtype, device):
+    """Raise ValueError unless tensor t has exactly this shape, dtype and
+    device and is contiguous: the C ABI receives raw pointers only and cannot
+    see the extent of a buffer, so a wrong one would be written or read past
+    its end."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def check_outputs(q, out, lse):
+    """The forward's o must match q (shape, dtype, device, contiguous) and lse
+    must be contiguous fp32 [B, H, N] on q's device; ValueError otherwise."""
+    import torch
+    B, H, N, _ = q.shape
+    _need(out, "out", q.shape, q.dtype, q.device)
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
+
+
 def attention(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     """Allocate o and lse with torch (when not given) and run the forward pass.
 
@@ -155,6 +182,8 @@ def attention(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None
         raise ValueError("q, k, v must all be bf16 or all fp32")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
+    if not (k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one device")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     B, H, N, d = q.shape
@@ -164,6 +193,7 @@ def attention(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    check_outputs(q, out, lse)
     fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
     st = fn(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
     if st != FA_OK:
@@ -185,6 +215,9 @@ def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=N
     if any(t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() for t in ts):
         raise ValueError("q, k, v, o, dout must be contiguous bf16 GPU tensors")
     B, H, N, d = q.shape
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
+    if any(t.device != q.device for t in ts):
+        raise ValueError("q, k, v, o, dout must be on one device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
@@ -207,6 +240,8 @@ def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=Non
         raise ValueError("q8, k8, v8 must share one [B, H, N, d] shape")
     if any(t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() for t in ts):
         raise ValueError("q8, k8, v8 must be contiguous uint8 GPU tensors")
+    if any(t.device != q8.device for t in ts):
+        raise ValueError("q8, k8, v8 must be on one device")
     B, H, N, d = q8.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -234,12 +269,16 @@ def decode_paged(q, k_cache, v_cache, page_table, seq_lens, scale=None, ws=None,
                   (page_table, torch.int32), (seq_lens, torch.int32)):
         if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
             raise ValueError("decode inputs must be contiguous CUDA tensors of the stated dtypes")
+        if t.device != q.device:
+            raise ValueError("decode inputs must be on one device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     max_pages = page_table.shape[1]
     need = fa_decode_workspace_bytes(B, H, d, page_size, max_pages)
     if ws is None:
         ws = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+    elif not isinstance(ws, torch.Tensor) or ws.device != q.device or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous tensor on q's device")
     o = torch.empty_like(q)
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     st = fa_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse, ws,

@@ -249,7 +249,9 @@ const char* fa_status_string(int status)
     case FA_ERR_ALIASING: return "an output overlaps an input or another output";
     case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case FA_ERR_TOO_LARGE: return "too many workgroups (B*H*ceil(N/128) >= 2^31)";
-    case FA_ERR_WORKSPACE: return "workspace NULL, not 256-byte aligned or too small";
+    case FA_ERR_WORKSPACE:
+        return "workspace NULL, misaligned (fa_decode_paged: 16 bytes; fa_std_*: 256 bytes) "
+               "or smaller than its *_workspace_bytes()";
     case FA_ERR_LIBRARY: return "a rocBLAS call failed";
     default: return "unknown status";
     }

@@ -213,3 +213,28 @@ def test_std_argument_errors():
     assert std.fa_std_softmax(A, A + 64 * MB + 2, A + 256 * MB, 1, 2, 100, 1) == 5
     assert std.fa_std_output(A, A + 64 * MB, A + 64 * MB, A + 512 * MB, 1, 2, 100, 64) == 6
     assert std.fa_std_output(A, A + 64 * MB, A + 128 * MB, A + 512 * MB, 1, 2, 100, 32) == 3
+
+
+def test_python_face_rejects_mismatched_outputs():
+    # The C ABI sees raw pointers only, so the Python face must refuse an
+    # out or lse buffer that does not have exactly the extent the kernels
+    # write: checked here on CPU tensors, before any launch could happen.
+    import torch
+    from io_aware_tiled_09_amd._binding import check_outputs
+    q = torch.zeros((2, 3, 40, 64), dtype=torch.float32)
+    good_o = torch.empty_like(q)
+    good_l = torch.empty((2, 3, 40), dtype=torch.float32)
+    check_outputs(q, good_o, good_l)
+    bad = [
+        (torch.empty_like(q, dtype=torch.bfloat16), good_l),          # fp32 q, bf16 out
+        (torch.empty((2, 3, 41, 64)), good_l),                         # wrong shape
+        (torch.empty((2, 3, 64, 40)).transpose(2, 3), good_l),         # not contiguous
+        (torch.empty_like(q, device="meta"), good_l),                  # other device
+        (good_o, torch.empty((2, 3, 40), dtype=torch.float64)),        # lse not fp32
+        (good_o, torch.empty((2, 3, 39), dtype=torch.float32)),        # lse too short
+        (good_o, torch.empty((2, 3, 40), dtype=torch.float32, device="meta")),
+        (good_o, torch.empty((3, 40, 2), dtype=torch.float32).permute(2, 0, 1)),
+    ]
+    for o, l in bad:
+        with pytest.raises(ValueError):
+            check_outputs(q, o, l)
