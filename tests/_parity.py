@@ -74,27 +74,35 @@ def check_rows(q, k, v, causal, scale, rows, label=""):
 # ---------------------------------------------------------------- backward pass
 # Bound on each gradient G in {dQ, dK, dV} against the oracle's R, per element
 # and relative to R's size (gradients have no natural unit):
-#   |G - R| <= GRAD_MAX_REL * (rms(R) + |R|)   and
-#   mean |G - R| <= GRAD_MEAN_REL * mean |R|   (denominators floored at GRAD_FLOOR).
+#   |G - R| <= max_rel * (rms(R) + |R|)   and
+#   mean |G - R| <= mean_rel * mean |R|   (denominators floored at GRAD_FLOOR),
+# rms and means taken over the whole array the test compares.
 # Where it comes from: the kernels round P and dS to bf16 (relative error up
-# to 2^-9) before their products, read O in bf16 for D = rowsum(dO * O), and
-# store the gradients in bf16; everything else is fp32. An fp32 CPU emulation
-# of exactly those rounding points on the tiny and ragged cases, and on single
-# heads with N = 512, 1024 (causal) and 2048 (causal, d = 128), gives at most
-# 0.046 for the per-element ratio and 0.0029 for the mean ratio; the bounds
-# are about twice that.
-#
-# D is formed from the stored bf16 O, as training frameworks hold it. Where a
-# few keys dominate a row (the spiky workload: 1% of K rows x20), P_ij is
-# close to 1 and dP_ij - D_i cancels to a small number, so O's rounding
-# (2^-9 relative) is a large relative error of dS and, times the large K
-# rows, of dQ and dK. The same emulation with the spiky workload's heads
-# gives 0.139 and 0.0101 (and 0.023 and 0.0022 with O unrounded, which
-# confirms the source); spiky inputs get GRAD_SPIKY_* instead.
+# to 2^-9) before their products (the dK/dV kernel forms its dS from the
+# already rounded P, a second rounding), read O in bf16 for
+# D = rowsum(dO * O), and store the gradients in bf16; everything else is
+# fp32. The fp32 model of
+# exactly those rounding points (tests/_emulate.py), run on the GPU tests' own
+# inputs, gives (tests/test_bounds.py):
+#  * tiny, ragged, explicit-scale and workload-head cases: at most 0.0440 for
+#    the per-element ratio and 0.00337 for the mean ratio -> GRAD_MAX_REL,
+#    GRAD_MEAN_REL (about 2.3x and 1.8x that);
+#  * the spiky workload's heads (1% of K rows x20): 0.1471 and 0.01023 ->
+#    GRAD_SPIKY_* (about 2x). Where a few keys dominate a row, P_ij is close
+#    to 1 and dP_ij - D_i cancels to a small number, so O's rounding (2^-9
+#    relative) is a large relative error of dS and, times the large K rows,
+#    of dQ and dK;
+#  * whole long causal heads (N = 8192, each head against its own rms):
+#    0.1164 (dQ), 0.1033 (dK) and 0.1026 (dV) -> GRAD_LONG_MAX_REL (1.7x).
+#    Early rows and keys of a causal head carry gradients far above the
+#    head's rms, so over 8192 rows the ratio reaches further into its tail
+#    than on short heads; the GPU reaches the model's figures at the same
+#    elements.
 GRAD_MAX_REL = 1e-1
 GRAD_MEAN_REL = 6e-3
 GRAD_SPIKY_MAX_REL = 3e-1
 GRAD_SPIKY_MEAN_REL = 2e-2
+GRAD_LONG_MAX_REL = 2e-1
 GRAD_FLOOR = 1e-3
 
 
@@ -107,23 +115,30 @@ def run_gpu_bwd(q, k, v, dout, causal, scale):
     return [t.double().cpu() for t in (dq, dk, dv)]
 
 
-def assert_grads_close(got, ref, label="", max_rel=None, mean_rel=None):
-    max_rel = GRAD_MAX_REL if max_rel is None else max_rel
-    mean_rel = GRAD_MEAN_REL if mean_rel is None else mean_rel
-    worst = {}
+def grad_errors(got, ref):
+    """The backward bound's two ratios per gradient: {name: {max_rel,
+    mean_rel, at}} for name in dq, dk, dv (empty arrays skipped)."""
+    out = {}
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         g = np.asarray(g, dtype=np.float64)
         assert g.shape == r.shape, (name, g.shape, r.shape)
-        assert np.isfinite(g).all(), f"non-finite GPU {name}"
+        assert np.isfinite(g).all(), f"non-finite {name}"
         if g.size == 0:
             continue
         d = np.abs(g - r)
         rms = max(float(np.sqrt((r * r).mean())), GRAD_FLOOR)
         mean_r = max(float(np.abs(r).mean()), GRAD_FLOOR)
         ratio = d / (rms + np.abs(r))
-        e = dict(max_rel=float(ratio.max()), mean_rel=float(d.mean()) / mean_r,
-                 at=np.unravel_index(int(ratio.argmax()), d.shape))
-        worst[name] = e
+        out[name] = dict(max_rel=float(ratio.max()), mean_rel=float(d.mean()) / mean_r,
+                         at=np.unravel_index(int(ratio.argmax()), d.shape))
+    return out
+
+
+def assert_grads_close(got, ref, label="", max_rel=None, mean_rel=None):
+    max_rel = GRAD_MAX_REL if max_rel is None else max_rel
+    mean_rel = GRAD_MEAN_REL if mean_rel is None else mean_rel
+    worst = grad_errors(got, ref)
+    for name, e in worst.items():
         say(f"  {label} {name}: max|d|/(rms+|R|)={e['max_rel']:.3e} "
             f"mean|d|/mean|R|={e['mean_rel']:.3e} worst at {e['at']}")
     for name, e in worst.items():
@@ -150,7 +165,7 @@ def check_bwd_full(q, k, v, dout, causal, scale, label="", heads=None, **bounds)
     return assert_grads_close(got, ref, label, **bounds)
 
 
-def check_bwd_sampled(q, k, v, dout, causal, scale, heads, qrows, krows, label=""):
+def check_bwd_sampled(q, k, v, dout, causal, scale, heads, qrows, krows, label="", **bounds):
     """Gradient parity on sampled heads, query rows (dQ) and key rows (dK, dV)."""
     got = run_gpu_bwd(q, k, v, dout, causal, scale)
     B, H, N, d = q.shape
@@ -161,4 +176,4 @@ def check_bwd_sampled(q, k, v, dout, causal, scale, heads, qrows, krows, label="
     for g, rows in zip(got, (qr, kr, kr)):
         gh = g.reshape(B * H, N, d)[hs]
         out.append(torch.gather(gh, 1, rows.unsqueeze(-1).expand(-1, -1, d)).numpy())
-    return assert_grads_close(out, ref, label)
+    return assert_grads_close(out, ref, label, **bounds)

@@ -1,0 +1,144 @@
+"""Where the derived parity bounds come from (CPU only).
+
+The pages fix no tolerance for the backward pass, and the forward's fixed
+bound (max 2e-2, mean 2e-3, lse 1e-3) says nothing about how much of it the
+kernel's own rounding uses. These tests run the fp32 model of the kernels'
+rounding points (tests/_emulate.py) on the GPU tests' own inputs, measure it
+against the fp64 oracle with the GPU tests' own metrics, and check that the
+figures quoted beside each bound in tests/_parity.py are what the model
+gives. A bound is then set above the model's figure on the same cases.
+
+On the cases where the GPU was run, the model reproduces the GPU's worst
+errors at the same elements: in the long-document heads 0 and 5, dQ 0.1164
+(head 0, row 6, column 43), dK 0.1033 and 0.1032 (key 0, column 70; key 1,
+column 98) and dV 0.1026 (head 0, key 0, column 40); on the spiky workload
+the forward's max |dO|, 0.0163 with a reference-max slack of 3.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_tiled_09_amd.inputs import WORKLOADS, make_dout, make_qkv
+
+import _emulate as E
+from _parity import (GRAD_LONG_MAX_REL, GRAD_MAX_REL, GRAD_MEAN_REL, GRAD_SPIKY_MAX_REL,
+                     GRAD_SPIKY_MEAN_REL, O_MAX_ABS, grad_errors)
+
+
+def _head(x, bh):
+    B, H, N, d = x.shape
+    return x.reshape(B * H, N, d)[bh].float().numpy()
+
+
+def _model_bwd_errors(q, k, v, do, causal, scale, heads=None):
+    """The backward model's errors on the given heads, with the GPU tests'
+    metric: {name: (max ratio, mean ratio, worst index)}."""
+    B, H, N, d = q.shape
+    heads = list(range(B * H)) if heads is None else heads
+    got, ref = [[], [], []], [[], [], []]
+    for bh in heads:
+        qh, kh, vh, dh = (_head(x, bh) for x in (q, k, v, do))
+        o, lse = E.flash_fwd(qh, kh, vh, scale, causal)
+        g = E.flash_bwd(qh, kh, vh, o, lse, dh, scale, causal)
+        r = oracle.attention_bwd(*(x[None, None] for x in (qh, kh, vh, dh)), scale, causal)
+        for i in range(3):
+            got[i].append(g[i].astype(np.float64))
+            ref[i].append(r[i][0, 0])
+    return grad_errors([np.stack(x) for x in got], [np.stack(x) for x in ref])
+
+
+def _small_backward_cases():
+    # the GPU backward tests' tiny, ragged, explicit-scale and workload cases
+    for N in [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 257]:
+        for d in (64, 128):
+            for causal in (False, True):
+                q, k, v = make_qkv(B=1, H=2, N=N, d=d, seed=N * 13 + d)
+                yield q, k, v, make_dout(B=1, H=2, N=N, d=d, seed=N * 13 + d), causal, d ** -0.5, None
+    for d in (64, 128):
+        for causal in (False, True):
+            q, k, v = make_qkv(B=2, H=3, N=333, d=d, seed=31 + d)
+            yield q, k, v, make_dout(B=2, H=3, N=333, d=d, seed=31 + d), causal, d ** -0.5, None
+    for scale in (0.05, 0.3):
+        q, k, v = make_qkv(B=1, H=3, N=300, d=64, seed=41)
+        yield q, k, v, make_dout(B=1, H=3, N=300, d=64, seed=41), True, scale, None
+    for name in ("bert512", "gpt2_1k"):
+        w = WORKLOADS[name]
+        q, k, v = make_qkv(w)
+        yield q, k, v, make_dout(w), w.causal, w.scale, [0, (w.B * w.H) // 2 + 1, w.B * w.H - 1]
+
+
+def test_backward_bound_small_cases():
+    worst_max = worst_mean = 0.0
+    for q, k, v, do, causal, scale, heads in _small_backward_cases():
+        for e in _model_bwd_errors(q, k, v, do, causal, scale, heads).values():
+            worst_max = max(worst_max, e["max_rel"])
+            worst_mean = max(worst_mean, e["mean_rel"])
+    print(f"model, small cases: max {worst_max:.4f} mean {worst_mean:.5f}")
+    # figures quoted in tests/_parity.py
+    assert abs(worst_max - 0.0440) < 1e-3
+    assert abs(worst_mean - 0.00337) < 5e-5
+    assert worst_max * 2.2 < GRAD_MAX_REL and worst_mean * 1.75 < GRAD_MEAN_REL
+
+
+def test_backward_bound_spiky():
+    w = WORKLOADS["gpt2_1k_spiky"]
+    q, k, v = make_qkv(w)
+    errs = _model_bwd_errors(q, k, v, make_dout(w), w.causal, w.scale,
+                             [0, (w.B * w.H) // 2 + 1, w.B * w.H - 1])
+    worst_max = max(e["max_rel"] for e in errs.values())
+    worst_mean = max(e["mean_rel"] for e in errs.values())
+    print(f"model, spiky heads: max {worst_max:.4f} mean {worst_mean:.5f}")
+    assert abs(worst_max - 0.1471) < 1e-3
+    assert abs(worst_mean - 0.01023) < 1e-4
+    assert worst_max * 2 < GRAD_SPIKY_MAX_REL and worst_mean * 1.9 < GRAD_SPIKY_MEAN_REL
+
+
+def test_backward_bound_long_causal_heads():
+    # The GPU test compares eight heads of the long-document workload in full
+    # (0, 5, 13, 31, 32, 42, 50, 63), each against its own rms; the model's
+    # largest per-head figures lie in heads 0 and 5, computed here (the GPU
+    # reached the same figures at the same elements in both heads). Early causal rows and keys carry gradients far above the head's
+    # rms, so the ratio's tail is longer than on the short heads above.
+    w = WORKLOADS["longdoc8k"]
+    q, k, v = make_qkv(w)
+    do = make_dout(w)
+    worst = {}
+    for bh in (0, 5):
+        for n, e in _model_bwd_errors(q, k, v, do, w.causal, w.scale, [bh]).items():
+            worst[n] = max(worst.get(n, 0.0), round(e["max_rel"], 4))
+            assert e["mean_rel"] * 2 < GRAD_MEAN_REL
+    print(f"model, long-document heads 0 and 5: {worst}")
+    assert worst == {"dq": 0.1164, "dk": 0.1033, "dv": 0.1026}
+    assert max(worst.values()) * 1.5 < GRAD_LONG_MAX_REL
+
+
+@pytest.mark.parametrize("slack,expect", [(0.0, 0.0153), (3.0, 0.0163), (8.0, 0.0263)])
+def test_forward_reference_max_slack_on_spiky_rows(slack, expect):
+    # The bf16 forward moves a row's reference max only when a tile's max
+    # passes it by more than 3 (base 2). On rows that one key dominates, that
+    # key's weight 2^delta is then rounded to bf16; the model gives the max
+    # |dO| the GPU measured for each slack (0.0153, 0.0163, 0.0263), and only
+    # the slack of 8 leaves the fixed bound of 2e-2.
+    w = WORKLOADS["gpt2_1k_spiky"]
+    q, k, v = make_qkv(w)
+    o_ref, _ = oracle.attention_fwd(q, k, v, w.scale, w.causal)
+    B, H, N, d = q.shape
+    worst = 0.0
+    for bh in range(B * H):
+        o, _ = E.flash_fwd(_head(q, bh), _head(k, bh), _head(v, bh), w.scale, w.causal,
+                           slack=slack)
+        worst = max(worst, float(np.abs(o - o_ref.reshape(B * H, N, d)[bh]).max()))
+    print(f"model, spiky forward, slack {slack}: max |dO| {worst:.4f}")
+    assert abs(worst - expect) < 1e-4
+    assert (worst <= O_MAX_ABS) == (slack <= 3.0)
+
+
+def test_emulated_bf16_rounding_is_round_to_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 1.0 - 2 ** -10],
+                 dtype=np.float32)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: the even mantissa (1) wins;
+    # 1 + 3*2^-8 ties between 1 + 2^-7 and 1 + 2^-6, and 1 + 2^-6 is even
+    want = np.array([1.0, 1.0, 1.0 + 2 ** -6, 1.0, -2.5, 1.0], dtype=np.float32)
+    np.testing.assert_array_equal(E.bf16(x).view(np.uint32), want.view(np.uint32))

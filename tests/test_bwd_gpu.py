@@ -9,8 +9,10 @@ import torch
 import io_aware_tiled_09_amd as fa
 from io_aware_tiled_09_amd.inputs import WORKLOADS, make_dout, make_qkv, sample_rows
 
-from _parity import (GRAD_SPIKY_MAX_REL, GRAD_SPIKY_MEAN_REL, check_bwd_full, check_bwd_sampled,
-                     run_gpu_bwd, say)
+import oracle
+
+from _parity import (GRAD_LONG_MAX_REL, GRAD_SPIKY_MAX_REL, GRAD_SPIKY_MEAN_REL, assert_grads_close,
+                     check_bwd_full, check_bwd_sampled, run_gpu_bwd, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +71,26 @@ def test_bwd_longdoc8k_sampled():
         f"{qrows.shape[1]} query rows and {krows.shape[1]} key rows each")
     q, k, v = make_qkv(w)
     check_bwd_sampled(q, k, v, make_dout(w), w.causal, w.scale, heads, qrows, krows,
-                      "longdoc8k")
+                      "longdoc8k", max_rel=GRAD_LONG_MAX_REL)
+
+
+def test_bwd_longdoc8k_full_heads():
+    # Every row of dQ, dK and dV in 8 of the 64 heads of the long-document
+    # workload (both batches, first, last and interior heads), from one
+    # fa_bwd call over the whole workload, against the materializing backward
+    # oracle, head by head (each head's own rms in the bound).
+    w = WORKLOADS["longdoc8k"]
+    heads = [0, 5, 13, 31, 32, 42, 50, 63]
+    say(f"bwd workload longdoc8k: every row of heads {heads}")
+    q, k, v = make_qkv(w)
+    do = make_dout(w)
+    got = run_gpu_bwd(q, k, v, do, w.causal, w.scale)
+    B, H, N, d = q.shape
+    for bh in heads:
+        sel = lambda x: x.reshape(B * H, N, d)[bh].reshape(1, 1, N, d)
+        ref = oracle.attention_bwd(sel(q), sel(k), sel(v), sel(do), w.scale, w.causal)
+        assert_grads_close([sel(g).numpy() for g in got], ref, f"longdoc8k head {bh}",
+                           max_rel=GRAD_LONG_MAX_REL)
 
 
 def test_bwd_deterministic_bitwise():

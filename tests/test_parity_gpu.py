@@ -14,7 +14,8 @@ import io_aware_tiled_09_amd as fa
 import oracle
 from io_aware_tiled_09_amd.inputs import WORKLOADS, make_qkv, sample_rows
 
-from _parity import assert_close, check_full, check_rows, run_gpu, say
+from _parity import (LSE_REL, O_MAX_ABS, O_MEAN_ABS, assert_close, check_full, check_rows,
+                     run_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +121,38 @@ def _rows_for(w, count):
     return torch.cat([rows, fixed.expand(w.B * w.H, -1)], dim=1)
 
 
+def test_workload_full_longdoc8k():
+    # Every output of the long-document workload (B=2, H=32, N=8192, d=128,
+    # causal): the GPU result of one fa_fwd call, in the launch configuration
+    # bench.py times, against the materializing oracle run head by head (one
+    # head's S and P, 2 x 512 MiB, at a time). The bound applies to the whole
+    # output: max and mean over all 64 x 8192 x 128 values, lse over all rows.
+    w = WORKLOADS["longdoc8k"]
+    say(f"workload longdoc8k, every row: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
+    q, k, v = make_qkv(w)
+    o_gpu, lse_gpu = run_gpu(q, k, v, w.causal, w.scale)
+    B, H, N, d = q.shape
+    o_max, o_sum, l_max, worst = 0.0, 0.0, 0.0, None
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, lse_ref = oracle.attention_fwd(q[sl], k[sl], v[sl], w.scale, w.causal)
+        dlt = np.abs(o_gpu[sl].numpy() - o_ref)
+        assert np.isfinite(dlt).all(), f"non-finite GPU output in head {bh}"
+        lrel = np.abs(lse_gpu[sl].numpy() - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)
+        if dlt.max() > o_max:
+            o_max = float(dlt.max())
+            worst = (b, h) + np.unravel_index(int(dlt.argmax()), dlt.shape)[2:]
+        o_sum += float(dlt.sum())
+        l_max = max(l_max, float(lrel.max()))
+        if bh % 16 == 15:
+            say(f"  heads 0..{bh}: max|dO|={o_max:.3e} lse rel={l_max:.3e}")
+    o_mean = o_sum / (B * H * N * d)
+    say(f"  longdoc8k, all rows: max|dO|={o_max:.3e} mean|dO|={o_mean:.3e} lse rel={l_max:.3e} "
+        f"worst O at {worst}")
+    assert o_max <= O_MAX_ABS and o_mean <= O_MEAN_ABS and l_max <= LSE_REL
+
+
 @pytest.mark.parametrize("name,count", [("longdoc8k", 48), ("longctx32k", 256)])
 def test_workload_sampled_rows(name, count):
     w = WORKLOADS[name]
@@ -206,6 +239,13 @@ def test_gpu_argument_errors():
     assert fa.fa_fwd(q, k, v, q, lse, 1, 1, 64, 64, 0.125, 0) == 6
     with pytest.raises(fa.FAError):
         fa.attention(q[..., :32].contiguous(), k[..., :32].contiguous(), v[..., :32].contiguous())
+    # buffers of the wrong extent are refused before any launch
+    with pytest.raises(ValueError):
+        fa.attention(q, k, v, out=torch.empty((1, 1, 32, 64), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.attention(q, k, v, lse=torch.empty((1, 1, 64), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.attention_backward(q, k, v, o, torch.empty((1, 1, 32), device="cuda"), q)
     torch.cuda.synchronize()
 
 
