@@ -23,8 +23,9 @@
  * contiguous [B][H][N] fp32 (the decode entry point documents its own
  * layout). Every pointer is a DEVICE pointer on the current HIP device. The
  * caller allocates and frees every buffer, workspaces included; the library
- * allocates nothing, frees nothing, keeps no state between calls and does
- * not synchronize.
+ * allocates nothing, frees nothing and does not synchronize. It keeps no
+ * state between calls, except the static scratch array of fa_bwd_noalloc
+ * (see there).
  *
  * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL means the
  * default stream) and the call returns once it is launched. Results are
@@ -56,7 +57,8 @@ typedef enum fa_status {
     FA_ERR_LAUNCH = 7,              /* the HIP runtime rejected the launch         */
     FA_ERR_TOO_LARGE = 8,           /* B*H*ceil(N/128) workgroups exceed 2^31 - 1  */
     FA_ERR_WORKSPACE = 9,           /* workspace NULL, misaligned or too small     */
-    FA_ERR_LIBRARY = 10             /* a library call (rocBLAS) failed             */
+    FA_ERR_LIBRARY = 10,            /* a library call (rocBLAS) failed             */
+    FA_ERR_SCRATCH_LIMIT = 11       /* B*H*N above fa_bwd_noalloc's static scratch */
 } fa_status;
 
 /*
@@ -107,6 +109,25 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            const float *lse, const void *dout, void *dq, void *dk, void *dv,
            float *ws, int B, int H, int N, int d, float scale, int causal,
            void *stream);
+
+/*
+ * The backward pass of fa_bwd for callers that cannot allocate: code being
+ * captured into a HIP graph, tight serving loops, and harnesses that forbid
+ * hipMalloc. Same arguments, results and checks as fa_bwd, without ws: the
+ * per-row D values live in a static device array of the library (16 MiB per
+ * GPU, held from the first call on that GPU until the process ends), so the
+ * call allocates and frees nothing. B*H*N must not exceed
+ * fa_bwd_noalloc_max_rows() (4,194,304; FA_ERR_SCRATCH_LIMIT otherwise).
+ * Every call on one GPU shares that array: calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialized by the caller.
+ * The first call on each GPU looks the array's device address up on the
+ * current device (no allocation).
+ */
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                   const float *lse, const void *dout, void *dq, void *dk,
+                   void *dv, int B, int H, int N, int d, float scale,
+                   int causal, void *stream);
+long long fa_bwd_noalloc_max_rows(void);
 
 /*
  * FP8 attention forward: Q, K and V as 8-bit E4M3 codes (OCP FP8 E4M3: 4

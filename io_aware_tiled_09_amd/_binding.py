@@ -20,9 +20,11 @@ STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEAD_DIM",
     4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_MISALIGNED", 6: "FA_ERR_ALIASING", 7: "FA_ERR_LAUNCH",
     8: "FA_ERR_TOO_LARGE", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_LIBRARY",
+    11: "FA_ERR_SCRATCH_LIMIT",
 }
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_decode_paged",
-           "fa_decode_workspace_bytes", "fa_status_string", "fa_tile_rows", "fa_tile_cols")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc",
+           "fa_bwd_noalloc_max_rows", "fa_decode_paged", "fa_decode_workspace_bytes",
+           "fa_status_string", "fa_tile_rows", "fa_tile_cols")
 
 
 class FAError(RuntimeError):
@@ -48,6 +50,10 @@ def load():
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, f, f, f, i, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_max_rows.argtypes = []
+    lib.fa_bwd_noalloc_max_rows.restype = ctypes.c_longlong
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_decode_paged.argtypes = [vp] * 8 + [ctypes.c_size_t] + [i] * 7 + [f, vp]
@@ -113,6 +119,21 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, d, scale, causal, str
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), int(B), int(H), int(N),
                              int(d), float(scale), int(bool(causal)),
                              _stream(stream, (q, k, v, o, lse, dout))))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                   stream=None) -> int:
+    """C fa_bwd_noalloc: fa_bwd without the workspace argument (the library's
+    static device scratch holds D; B*H*N <= fa_bwd_noalloc_max_rows()).
+    Returns the fa_status code."""
+    return int(load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), int(B), int(H), int(N),
+                                     int(d), float(scale), int(bool(causal)),
+                                     _stream(stream, (q, k, v, o, lse, dout))))
+
+
+def fa_bwd_noalloc_max_rows() -> int:
+    return int(load().fa_bwd_noalloc_max_rows())
 
 
 def fa_decode_workspace_bytes(B, H, d, page_size, max_pages) -> int:

@@ -17,6 +17,7 @@ SOURCES = [os.path.join(PKG, "csrc", "fa_fwd_bf16.hip"),
            os.path.join(PKG, "csrc", "fa_fwd_f32.hip"),
            os.path.join(PKG, "csrc", "fa_fwd_fp8.hip"),
            os.path.join(PKG, "csrc", "fa_decode.hip"),
+           os.path.join(PKG, "csrc", "fa_scratch.hip"),
            os.path.join(PKG, "csrc", "fa_api.cpp")]
 ARCH = "gfx950"
 

@@ -194,15 +194,26 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-           const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N, int d,
-           float scale, int causal, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two backward entry points. ws == NULL: the workspace
+// is the library's static scratch (fa_bwd_noalloc), which no caller buffer
+// can overlap.
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, const void* dq, const void* dk, const void* dv,
+                 const float* ws, bool need_ws, int B, int H, int N, int d, float scale,
+                 bool* empty)
 {
+    *empty = false;
     if (B < 0 || H < 0 || N < 0)
         return FA_ERR_BAD_SHAPE;
-    if (B == 0 || H == 0 || N == 0)
+    if (B == 0 || H == 0 || N == 0) {
+        *empty = true;
         return FA_OK;
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws)
+    }
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || (need_ws && !ws))
         return FA_ERR_NULL_PTR;
     if (d != 64 && d != 128)
         return FA_ERR_UNSUPPORTED_HEAD_DIM;
@@ -222,7 +233,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
                          {addr(v), addr(v) + tb},     {addr(o), addr(o) + tb},
                          {addr(lse), addr(lse) + rb}, {addr(dout), addr(dout) + tb}};
     const Range out[4] = {{addr(dq), addr(dq) + tb}, {addr(dk), addr(dk) + tb},
-                          {addr(dv), addr(dv) + tb}, {addr(ws), addr(ws) + rb}};
+                          {addr(dv), addr(dv) + tb}, {addr(ws), addr(ws) + (need_ws ? rb : 0)}};
     for (int a = 0; a < 4; ++a) {
         for (int b = 0; b < 6; ++b)
             if (overlaps(out[a], in[b]))
@@ -231,11 +242,49 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
             if (overlaps(out[a], out[b]))
                 return FA_ERR_ALIASING;
     }
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N, int d,
+           float scale, int causal, void* stream)
+{
+    bool empty;
+    const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, true, B, H, N, d, scale,
+                                &empty);
+    if (st != FA_OK || empty)
+        return st;
     const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, ws, B * H, N, d,
                                              kernel_scale(scale), scale, causal != 0,
                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float scale, int causal, void* stream)
+{
+    bool empty;
+    const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, false, B, H, N, d,
+                                scale, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    if ((long long)B * H * N > fa::kBwdScratchRows)
+        return FA_ERR_SCRATCH_LIMIT;
+    float* ws = nullptr;
+    if (fa::bwd_scratch(&ws) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, ws, B * H, N, d,
+                                             kernel_scale(scale), scale, causal != 0,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+long long fa_bwd_noalloc_max_rows(void) { return fa::kBwdScratchRows; }
 
 const char* fa_status_string(int status)
 {
@@ -253,6 +302,8 @@ const char* fa_status_string(int status)
         return "workspace NULL, misaligned (fa_decode_paged: 16 bytes; fa_std_*: 256 bytes) "
                "or smaller than its *_workspace_bytes()";
     case FA_ERR_LIBRARY: return "a rocBLAS call failed";
+    case FA_ERR_SCRATCH_LIMIT:
+        return "B*H*N exceeds the static scratch of fa_bwd_noalloc (fa_bwd_noalloc_max_rows())";
     default: return "unknown status";
     }
 }

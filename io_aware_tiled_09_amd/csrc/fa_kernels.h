@@ -23,6 +23,13 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            float* delta, int BH, int N, int d, float scale_log2, float scale,
                            bool causal, hipStream_t stream);
 
+// Static device scratch of the allocation-free backward (fa_scratch.hip):
+// room for the D values of B*H*N <= kBwdScratchRows rows (16 MiB per GPU).
+// bwd_scratch() returns the current device's address of it, looked up once
+// per device; it allocates nothing.
+constexpr long long kBwdScratchRows = 1LL << 22;
+hipError_t bwd_scratch(float** out);
+
 // FP8 E4M3 forward (d = 128): q, k, v hold E4M3 codes; c_log2 = scale *
 // q_scale * k_scale * log2(e) > 0; out_scale = v_scale.
 hipError_t launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert fa.fa_status_string(0) == "ok"
-    for code in range(1, 11):
+    for code in range(1, 12):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -158,6 +158,36 @@ def test_bwd_argument_errors():
     assert _bwd(B=65536, H=65536, N=128) == 8
     for B, H, N in ((0, 4, 100), (2, 0, 100), (2, 4, 0)):
         assert fa.fa_bwd(*([None] * 10), B, H, N, 64, 0.125, 1, None) == 0
+
+
+def _bwd_na(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+            dout=A + 320 * MB, dq=A + 384 * MB, dk=A + 448 * MB, dv=A + 512 * MB,
+            B=1, H=2, N=100, d=64, scale=0.125, causal=0):
+    return fa.fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, 0)
+
+
+def test_bwd_noalloc_argument_errors():
+    # every check runs before the static scratch is looked up or anything is
+    # launched
+    assert fa.fa_bwd_noalloc_max_rows() == 4194304
+    assert _bwd_na(dout=0) == 1
+    assert _bwd_na(N=-1) == 2
+    assert _bwd_na(d=32) == 3
+    assert _bwd_na(scale=float("inf")) == 4
+    assert _bwd_na(dq=A + 384 * MB + 8) == 5
+    assert _bwd_na(lse=A + 256 * MB + 2) == 5
+    assert _bwd_na(dq=A) == 6
+    assert _bwd_na(dv=A + 448 * MB) == 6
+    # one row past the static scratch: 4194305 rows of d = 64 (512 MiB per
+    # tensor, addresses 1 GiB apart)
+    G = 1024 * MB
+    big = dict(q=A, k=A + G, v=A + 2 * G, o=A + 3 * G, lse=A + 4 * G, dout=A + 5 * G,
+               dq=A + 6 * G, dk=A + 7 * G, dv=A + 8 * G)
+    assert _bwd_na(B=1, H=1, N=4194305, **big) == 11
+    assert _bwd_na(B=2, H=1, N=2097153, **big) == 11
+    assert "static scratch" in fa.fa_status_string(11)
+    for B, H, N in ((0, 4, 100), (2, 0, 100), (2, 4, 0)):
+        assert fa.fa_bwd_noalloc(*([None] * 9), B, H, N, 64, 0.125, 1, None) == 0
 
 
 # ---------------------------------------------------------------- libfa_std.so
