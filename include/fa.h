@@ -142,7 +142,8 @@ long long fa_bwd_noalloc_max_rows(void);
  * d == 128 only (FA_ERR_UNSUPPORTED_HEAD_DIM otherwise); scale >= 0 and
  * finite; q_scale, k_scale, v_scale > 0 and finite (FA_ERR_BAD_SCALE).
  * Both products run on the FP8 matrix instructions with fp32 accumulation;
- * the softmax weights are rounded to E4M3 (as 256 p) for the second product.
+ * the softmax weights are rounded to E4M3 (as 48 p, p <= 8) for the second
+ * product.
  * Codes 0x7F and 0xFF (NaN) propagate as NaN.
  */
 int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -110,3 +110,48 @@ def flash_bwd(q, k, v, o, lse, dout, scale, causal):
     del P
     dk = bf16((bf16(Pb * dP).T @ np.asarray(q, F32)) * F32(scale))
     return dq, dk, dv
+
+
+def e4m3(x) -> np.ndarray:
+    """Round non-negative float32 values to the nearest OCP FP8 E4M3 value
+    (ties to even): 3 mantissa bits in the normal range [2^-6, 448],
+    multiples of 2^-9 below it. Values above 448 are not expected."""
+    x = np.ascontiguousarray(x, dtype=F32)
+    u = x.view(np.uint32)
+    normal = (u + np.uint32(0x7FFFF) + ((u >> np.uint32(20)) & np.uint32(1))) & np.uint32(0xFFF00000)
+    sub = (np.round(x.astype(np.float64) * 512.0) / 512.0).astype(F32)
+    return np.where(x >= F32(2.0 ** -6), normal.view(F32), sub).astype(F32)
+
+
+def flash_fwd_fp8(q, k, v, scale, causal, tile=128, slack=3.0, pscale=48.0):
+    """The FP8 forward kernel's arithmetic on decoded inputs (q, k, v already
+    q_scale * code etc., as float32): key tiles of `tile`; scores in fp32
+    (exact products of 8-bit values, fp32 sums); per row a reference max
+    (base 2) moved only when a tile's max passes it by more than `slack`;
+    w = exp2(fma(s, c, -(m - log2 pscale))) = pscale * p in fp32, summed in
+    fp32; P for the product with V rounded to E4M3 as w; the output rescaled
+    when the reference moves; O = acc / l rounded to bf16 (the codes' v scale
+    is in v already); lse = (m + log2(l / pscale)) * ln 2."""
+    N, d = q.shape
+    c = kernel_c(scale)
+    S = scores(q, k, causal)
+    lg = F32(np.log2(pscale))
+    m = np.full(N, -np.inf, F32)
+    l = np.zeros(N, F32)
+    acc = np.zeros((N, d), F32)
+    for t0 in range(0, N, tile):
+        s = S[:, t0:t0 + tile]
+        raw = s.max(axis=1)
+        mt = np.where(raw > -np.inf, raw * c, -np.inf).astype(F32)
+        grow = mt > m + F32(slack)
+        m_new = np.where(grow, mt, m).astype(F32)
+        with np.errstate(invalid="ignore"):
+            alpha = np.exp2(np.where(np.isfinite(m), m - m_new, -np.inf)).astype(F32)
+        m = m_new
+        w = np.exp2(fma32(s, c, -(m - lg)[:, None])).astype(F32)
+        l = (l * alpha + w.sum(axis=1, dtype=F32)).astype(F32)
+        acc = (acc * alpha[:, None]).astype(F32)
+        acc = (acc + e4m3(w) @ np.asarray(v[t0:t0 + tile], F32)).astype(F32)
+    o = bf16(acc * (F32(1.0) / l)[:, None])
+    lse = ((m + np.log2(l / F32(pscale)).astype(F32)) * F32(LN2)).astype(F32)
+    return o, lse

@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
-from io_aware_tiled_09_amd.inputs import WORKLOADS, make_dout, make_qkv
+from io_aware_tiled_09_amd.inputs import WORKLOADS, make_dout, make_qkv, make_qkv_fp8
 
 import _emulate as E
 from _parity import (GRAD_LONG_MAX_REL, GRAD_MAX_REL, GRAD_MEAN_REL, GRAD_SPIKY_MAX_REL,
@@ -142,3 +142,54 @@ def test_emulated_bf16_rounding_is_round_to_nearest_even():
     # 1 + 3*2^-8 ties between 1 + 2^-7 and 1 + 2^-6, and 1 + 2^-6 is even
     want = np.array([1.0, 1.0, 1.0 + 2 ** -6, 1.0, -2.5, 1.0], dtype=np.float32)
     np.testing.assert_array_equal(E.bf16(x).view(np.uint32), want.view(np.uint32))
+
+
+def _fp8_cases():
+    # the FP8 GPU tests' cases (tests/test_fp8_gpu.py), all but the sampled
+    # long-document rows
+    for N in [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 257, 333]:
+        for causal in (False, True):
+            yield make_qkv_fp8(B=1, H=2, N=N, d=128, seed=N * 5 + 1), causal, 128 ** -0.5
+    for name in ("gpt2_1k", "gpt2_1k_spiky"):
+        yield make_qkv_fp8(name, B=2, H=4, d=128), True, 128 ** -0.5
+    codes, sc = make_qkv_fp8(B=1, H=3, N=300, d=128, seed=77)
+    yield (codes, (sc[0] * 3.0, sc[1] * 0.5, sc[2] * 2.0)), True, 0.3
+
+
+def test_fp8_bound():
+    # The FP8 model (E4M3 weights w = 48 p with a reference-max slack of 3,
+    # bf16 output) against the oracle on the decoded inputs, with the FP8
+    # test's per-element bound 2^-4 sum_j P|V| + 2^-8 |O| + 1e-4.
+    worst = mean_ratio = excess = lse = 0.0
+    for (codes, scales), causal, scale in _fp8_cases():
+        deq = [oracle.decode_e4m3(c, s) for c, s in zip(codes, scales)]
+        o_ref, l_ref = oracle.attention_fwd(*deq, scale, causal)
+        a_ref, _ = oracle.attention_fwd(deq[0], deq[1], np.abs(deq[2]), scale, causal)
+        B, H, N, d = deq[0].shape
+        for bh in range(B * H):
+            f = lambda a: a.reshape(B * H, N, d)[bh].astype(np.float32)
+            o, l_ = E.flash_fwd_fp8(f(deq[0]), f(deq[1]), f(deq[2]), scale, causal)
+            o_r, a_r = o_ref.reshape(B * H, N, d)[bh], a_ref.reshape(B * H, N, d)[bh]
+            rel = 2.0 ** -4 * a_r + 2.0 ** -8 * np.abs(o_r)
+            dd = np.abs(o - o_r)
+            worst = max(worst, float((dd / (rel + 1e-4)).max()))
+            mean_ratio = max(mean_ratio, float(dd.mean() / (rel + 1e-4).mean()))
+            excess = max(excess, float((dd - rel).max()))
+            lr = l_ref.reshape(B * H, N)[bh]
+            lse = max(lse, float((np.abs(l_ - lr) / np.maximum(np.abs(lr), 1.0)).max()))
+    print(f"FP8 model: max {worst:.3f} of the bound, mean ratio {mean_ratio:.3f}, "
+          f"excess over the relative terms {excess:.2e}, lse {lse:.2e}")
+    # figures quoted in tests/test_fp8_gpu.py
+    assert abs(worst - 0.892) < 2e-3 and abs(mean_ratio - 0.166) < 2e-3
+    assert excess < 3e-5 < 1e-4 and lse < 1e-5
+
+
+def test_fp8_weight_scale_leaves_room_for_the_slack():
+    # w = 48 p with p <= 2^3 stays below the largest E4M3 value, 448, and the
+    # model's E4M3 rounding agrees with torch's float8_e4m3fn conversion.
+    import torch
+    assert 48.0 * 2.0 ** 3 <= 448.0 < 48.0 * 2.0 ** 3.3
+    x = np.abs(np.random.default_rng(0).normal(0, 40, 100000)).astype(np.float32)
+    x = x[x <= 448.0]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(E.e4m3(x), ref)
