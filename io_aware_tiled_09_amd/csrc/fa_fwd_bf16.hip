@@ -56,6 +56,9 @@
 //  * Causal: key tiles past the workgroup's last query are never loaded, a
 //    wave skips tiles that lie wholly above its 32 rows, and the mask is
 //    applied only on tiles that cross a wave's diagonal or the sequence end.
+//    The tiles below the workgroup's diagonal run as straight-line steps
+//    without those conditions, each phase one basic block whose crossing
+//    values are pinned on both sides of the barrier.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -261,16 +264,21 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         }
     };
     // Replace the scores of invisible keys (past N, or after the query when
-    // causal) by -inf.
+    // causal) by -inf. Key score_key(st, r, lh) of the tile is visible iff
+    // its lane-independent part st*32 + (r/4)*8 + r%4, a compile-time
+    // constant, is at most one per-lane limit: written with per-key indices,
+    // the mask had the compiler keep all 32 key indices in registers.
     auto mask = [&](int kb, f32x16 (&s)[kBc / 32]) {
-        const int j0 = kb * kBc;
+        int lim = N - 1 - kb * kBc;
+        if constexpr (CAUSAL) lim = min(lim, qi - kb * kBc);
+        lim -= lh * 4;
+        asm volatile("" : "+v"(lim));
 #pragma unroll
         for (int st = 0; st < kBc / 32; ++st)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = j0 + score_key(st, r, lh);
-                const bool ok = j < N && (!CAUSAL || j <= qi);
-                s[st][r] = ok ? s[st][r] : neg_inf();
+                const int kc = st * 32 + (r >> 2) * 8 + (r & 3);
+                s[st][r] = kc <= lim ? s[st][r] : neg_inf();
             }
     };
 
@@ -344,9 +352,12 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // A(j): VALU only. Softmax of tile j (scores in sc): reference max and
     // running sum, bf16 P, and O *= alpha (skipped when no row's reference
     // moved: alpha == 1).
-    auto phase_a = [&](int kb) __attribute__((always_inline)) {
-        if (kb > last) return;
-        if (kb >= nfull_w) mask(kb, sc);
+    auto phase_a = [&](auto full, int kb) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full)::value;
+        if (!FULL) {
+            if (kb > last) return;
+            if (kb >= nfull_w) mask(kb, sc);
+        }
         // Row max of the lane's 32 scores in four v_max3 chains, then with the
         // partner lane. The scores are finite or -inf; written as instructions
         // because fmaxf would add a canonicalizing move per MFMA result.
@@ -410,9 +421,10 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     constexpr int kPVMfmas = D / 32 * kBc / 16;
     // B(j): MFMA work only. Scores of tile j+1 from K ring slot kslot, then
     // O^T += V_j^T P_j^T from V ring slot vslot.
-    auto phase_b = [&](int kb, int kslot, int vslot) __attribute__((always_inline)) {
+    auto phase_b = [&](auto full, int kb, int kslot, int vslot) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full)::value;
         if constexpr (PAIRED) asm volatile("" : "+v"(k_off[0]), "+v"(v_off[0][0]), "+v"(v_off[0][1]));
-        if (kb + 1 <= last) {
+        if (FULL || kb + 1 <= last) {
             scores(kslot, sc);
             // K fragments kReadAhead MFMAs ahead, no further (VGPR budget).
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadAhead, 0);
@@ -423,7 +435,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             }
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, kReadAhead, 0);
         }
-        if (kb > last) return;
+        if (!FULL && kb > last) return;
         // 16-key chunk outer, 32-column block inner: consecutive MFMAs update
         // different accumulators.
 #pragma unroll
@@ -451,27 +463,85 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, kReadAhead, 0);
     };
+    // The values that cross a phase boundary pass through empty volatile asm
+    // on both sides of its barrier, so that their producers stay in the phase
+    // that ends and their consumers in the phase that starts (the compiler
+    // sees no dependence on the barrier and otherwise moves pure arithmetic,
+    // P.V MFMAs or the next exponentials, across it): A -> B: P, m, l;
+    // B -> A: the next tile's scores and the output accumulators.
+    auto pin_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) asm volatile("" : "+v"(pf[st][0]), "+v"(pf[st][1]));
+        asm volatile("" : "+v"(m_run), "+v"(l_run));
+    };
+    auto pin_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) asm volatile("" : "+v"(sc[st]));
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) asm volatile("" : "+v"(acc[t]));
+    };
     // Tile j as this wave sees it: A(j) then B(j), each in its global phase
     // (group 1 one phase later than group 0). R = j mod 4 is a compile-time
-    // constant, so every ring slot is a fixed LDS offset.
+    // constant, so every ring slot is a fixed LDS offset. This general step
+    // keeps the per-wave conditions (tiles past the wave's last one, masked
+    // tiles, the partial tile's clear); pinning here as well measured even.
     auto step = [&](auto ring, int kb) __attribute__((always_inline)) {
         constexpr int R = decltype(ring)::value;
         const int s = 2 * kb + grp;
         phase_loads(s);
-        phase_a(kb);
+        phase_a(std::false_type{}, kb);
         phase_end(s);
         phase_loads(s + 1);
-        phase_b(kb, (R + 1) & 3, R);
+        phase_b(std::false_type{}, kb, (R + 1) & 3, R);
         phase_end(s + 1);
+    };
+    // Steps that every wave runs whole (tiles j and j + 1 below the
+    // workgroup's first query when causal, inside N, and before the phase of
+    // the partial tile's clear) as straight-line code: no mask, no skip, and
+    // the loads without a branch (phase 2 kb + grp is always this wave's
+    // loading phase: group 0 loads V_{kb+2}, group 1 K_{kb+4}). With the
+    // pins, one basic block per phase: 4.5% faster on the long-document
+    // workload, 8% on non-causal N = 4096, bitwise-equal outputs.
+    auto phase_end_plain = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * L));
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto step_full = [&](auto ring, int kb) __attribute__((always_inline)) {
+        constexpr int R = decltype(ring)::value;
+        {
+            const bool isk = grp != 0;
+            issue_grp(isk ? kh : vh, kb + (isk ? 4 : 2), isk ? kring[R] : vring[(R + 2) & 3]);
+        }
+        phase_a(std::true_type{}, kb);
+        pin_a();
+        phase_end_plain();
+        pin_a();
+        phase_b(std::true_type{}, kb, (R + 1) & 3, R);
+        pin_b();
+        phase_end_plain();
+        pin_b();
     };
 
     if (grp == 1) {  // group 1's idle first phase
         phase_loads(0);
         phase_end(0);
     }
+    // Steps j < kb_full are full; kb_full <= nkb - 2 keeps the phase of the
+    // partial tile's clear (2 nkb - 2, which group 1 reaches in step nkb - 2)
+    // in the general path for both groups, so both meet its extra barrier.
+    int kb = 0;
+    const int kb_full = min(CAUSAL ? q0 / kBc : nkb - 1, min(N / kBc, nkb - 2));
+    for (; kb + 4 <= kb_full; kb += 4) {
+        step_full(std::integral_constant<int, 0>{}, kb);
+        step_full(std::integral_constant<int, 1>{}, kb + 1);
+        step_full(std::integral_constant<int, 2>{}, kb + 2);
+        step_full(std::integral_constant<int, 3>{}, kb + 3);
+    }
     // Four tiles per iteration; steps past the last tile (kb >= nkb) only
     // issue their (empty) loads and meet the barriers.
-    for (int kb = 0; kb < nkb; kb += 4) {
+    for (; kb < nkb; kb += 4) {
         step(std::integral_constant<int, 0>{}, kb);
         step(std::integral_constant<int, 1>{}, kb + 1);
         step(std::integral_constant<int, 2>{}, kb + 2);
