@@ -1,6 +1,6 @@
 // C ABI of the attention-forward library: argument checks, then one kernel
 // launch on the caller's stream. See include/fa.h for the contract.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <float.h>
 #include <math.h>
 #include <stddef.h>

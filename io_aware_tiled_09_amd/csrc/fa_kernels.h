@@ -1,6 +1,6 @@
 // Internal interface between the C ABI layer and the gfx950 kernels.
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 namespace fa {
 
