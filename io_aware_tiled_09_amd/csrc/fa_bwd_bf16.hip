@@ -45,6 +45,7 @@ constexpr int kBwdRows = kBwdWaves * 32;     // queries (dq) or keys (dkdv) per 
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kDqReadAhead = 4;
+constexpr int kDkdvReadAhead = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- delta
@@ -122,12 +123,13 @@ __device__ inline void clear_tile_tail(int t, int N, unsigned char* dst, int tid
 // Each wave holds one 32x128 accumulator and one operand set (about half the
 // registers of a wave doing both), so two waves fit per SIMD; waves w and
 // w + 4 share a SIMD and serve different key groups.
-// The pair is software-pipelined by one tile: in step t the P-wave does
-// dV(t) then S(t+1), P(t+1), and the dS-wave does dS(t), dK(t) then dP(t+1).
-// Each wave's MFMA runs then sit next to the other wave's VALU work
-// (exponentials at the P-wave's end, dS at the dS-wave's start), and one
-// barrier per tile publishes both P(t+1) and the next Q/dO tile. Q and dO
-// tiles use three LDS buffers (t, t+1 in use, t+2 loading), P two.
+// The pair is software-pipelined by one tile and each step has two phases:
+// in phase 1 the P-wave runs dV(t) and S(t+1) on the matrix core while the
+// dS-wave forms dS(t); in phase 2 the dS-wave runs dK(t) and dP(t+1) while the
+// P-wave forms P(t+1). On every SIMD one wave of the pair feeds the matrix
+// core while the other works on the VALU, and the barrier between the phases
+// also orders the reads of P(t) before the writes of P(t+1), so P needs one
+// LDS buffer. Q and dO tiles use three (t, t+1 in use, t+2 loading).
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * 64;
 
@@ -147,7 +149,7 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     __shared__ __attribute__((aligned(16))) float dl_s[3][kBc];   // D per query
     // P of a tile per key group: [tile & 1][group][sub-tile][half][lane] x 8
     // bf16 (lane-major 16-byte slots, conflict-free).
-    __shared__ __attribute__((aligned(16))) bf16x8 p_x[2][kBwdWaves][kBc / 32][2][64];
+    __shared__ __attribute__((aligned(16))) bf16x8 p_x[kBwdWaves][kBc / 32][2][64];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,14 +186,11 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     int ld_off[L];
 #pragma unroll
     for (int it = 0; it < L; ++it) ld_off[it] = TL::load_offset(wave, it, lane);
-    int f_off[D / 16];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) f_off[c] = TL::frag_offset(li, 2 * c + lh);
-    int t_off[D / 32][2];
-#pragma unroll
-    for (int tt = 0; tt < D / 32; ++tt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) t_off[tt][s] = TL::tr_offset(tt, s, lane);
+    // Fragment and transpose-read offsets from two bases: chunk 2c + lh of a
+    // row sits at base ^ (c << 5), and the transpose reads of column block tt
+    // at base ^ (tt << 6) (the swizzle XORs only chunk bits).
+    const int f_base = TL::frag_offset(li, lh);
+    const int t_base[2] = {TL::tr_offset(0, 0, lane), TL::tr_offset(0, 1, lane)};
 
     const int nqt = (N + kBc - 1) / kBc;
     // Causal: query tiles before the block's first key see none of its keys.
@@ -204,6 +203,9 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         return (CAUSAL && u * kBc < kw0 + 31) || u * kBc + kBc > N;
     };
 
+    // Tile u of the block's range lives in slot (u - t0) % 3 of the Q, dO
+    // and statistics buffers; the straight-line steps below take their slots
+    // as compile-time constants.
     // Per-query statistics of tile u: threads 0..63 fetch lse, 64..127 D.
     auto fetch_stats = [&](int u) __attribute__((always_inline)) {
         const int qq = u * kBc + (tid & 63);
@@ -211,43 +213,51 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         if (tid < 2 * kBc && qq < N) x = tid < kBc ? lseh[qq] * kLog2e : dlh[qq];
         return x;
     };
-    auto put_stats = [&](int u, float x) __attribute__((always_inline)) {
-        if (tid < kBc) lse_s[u % 3][tid] = x;
-        else if (tid < 2 * kBc) dl_s[u % 3][tid - kBc] = x;
+    auto put_stats = [&](int sl, float x) __attribute__((always_inline)) {
+        if (tid < kBc) lse_s[sl][tid] = x;
+        else if (tid < 2 * kBc) dl_s[sl][tid - kBc] = x;
     };
-    auto load_tile = [&](int u) __attribute__((always_inline)) {
-        issue_tile<TL>(qh, u, N, qbuf[u % 3], ld_off, wave);
-        issue_tile<TL>(doh, u, N, dobuf[u % 3], ld_off, wave);
+    auto load_tile = [&](int u, int sl) __attribute__((always_inline)) {
+        issue_tile<TL>(qh, u, N, qbuf[sl], ld_off, wave);
+        issue_tile<TL>(doh, u, N, dobuf[sl], ld_off, wave);
     };
-    auto clear_tails = [&](int u) __attribute__((always_inline)) {
-        clear_tile_tail<TL, kDkdvThreads>(u, N, qbuf[u % 3], tid);
-        clear_tile_tail<TL, kDkdvThreads>(u, N, dobuf[u % 3], tid);
+    auto clear_tails = [&](int u, int sl) __attribute__((always_inline)) {
+        clear_tile_tail<TL, kDkdvThreads>(u, N, qbuf[sl], tid);
+        clear_tile_tail<TL, kDkdvThreads>(u, N, dobuf[sl], tid);
     };
 
-    // S (P-wave, from Q) or dP (dS-wave, from dO) of tile u: lane = key, 16
-    // queries per 32-query sub-tile.
+    // S (P-wave, from Q) or dP (dS-wave, from dO) of the tile in slot sl:
+    // lane = key, 16 queries per 32-query sub-tile. The A fragments are read
+    // kDkdvReadAhead MFMAs ahead of their use.
     f32x16 x[kBc / 32];
-    auto scores = [&](int u) __attribute__((always_inline)) {
-        const unsigned char* at = pwave ? qbuf[u % 3] : dobuf[u % 3];
+    auto scores = [&](auto role, int sl) __attribute__((always_inline)) {
+        const unsigned char* at = decltype(role)::value ? qbuf[sl] : dobuf[sl];
 #pragma unroll
         for (int st = 0; st < kBc / 32; ++st) {
             x[st] = f32x16{};
 #pragma unroll
             for (int c = 0; c < D / 16; ++c)
                 x[st] = mfma(*reinterpret_cast<const bf16x8*>(at + st * 32 * TL::kRowBytes +
-                                                              f_off[c]),
+                                                              (f_base ^ (c << 5))),
                              bf[c], x[st]);
         }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDkdvReadAhead, 0);
+#pragma unroll
+        for (int i = 0; i < kBc / 32 * D / 16 - kDkdvReadAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kDkdvReadAhead, 0);
     };
-    // P-wave: P = exp2(s c - lse2_q) of tile u, 0 where masked, into pf and
-    // p_x[u & 1]. Query qloc + i of the tile is valid for this lane's key iff
+    // P-wave: P = exp2(s c - lse2) of tile u (slot sl), 0 where masked, into
+    // pf and p_x. Query qloc + i of the tile is valid for this lane's key iff
     // lo <= qloc + i < hi (one unsigned compare); tiles that need no mask
     // take a separate path without it.
     bf16x8 pf[kBc / 32][2];
-    auto probs = [&](int u) __attribute__((always_inline)) {
+    auto probs = [&](int u, int sl, auto nomask) __attribute__((always_inline)) {
         const int lo = CAUSAL ? kj - u * kBc : 0;
         const int hi = N - u * kBc;
-        const float* ls = lse_s[u % 3];
+        const float* ls = lse_s[sl];
         auto run = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
             for (int st = 0; st < kBc / 32; ++st) {
@@ -265,20 +275,20 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                         pf[st][r >> 3][r & 7] = (__bf16)p;
                     }
                 }
-                p_x[u & 1][grp][st][0][lane] = pf[st][0];
-                p_x[u & 1][grp][st][1][lane] = pf[st][1];
+                p_x[grp][st][0][lane] = pf[st][0];
+                p_x[grp][st][1][lane] = pf[st][1];
             }
         };
-        if (need_mask(u)) run(std::true_type{});
+        if (!decltype(nomask)::value && need_mask(u)) run(std::true_type{});
         else run(std::false_type{});
     };
-    // dS-wave: dS = P (dP - D_q) of tile u into pf, P from the partner.
-    auto dscores = [&](int u) __attribute__((always_inline)) {
-        const float* ds_ = dl_s[u % 3];
+    // dS-wave: dS = P (dP - D) of the tile in slot sl into pf, P from the partner.
+    auto dscores = [&](int sl) __attribute__((always_inline)) {
+        const float* ds_ = dl_s[sl];
 #pragma unroll
         for (int st = 0; st < kBc / 32; ++st) {
-            const bf16x8 p0 = p_x[u & 1][grp][st][0][lane];
-            const bf16x8 p1 = p_x[u & 1][grp][st][1][lane];
+            const bf16x8 p0 = p_x[grp][st][0][lane];
+            const bf16x8 p1 = p_x[grp][st][1][lane];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int qloc = st * 32 + g * 8 + lh * 4;
@@ -295,10 +305,10 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (dS-wave): rows d, column = key
 #pragma unroll
     for (int tt = 0; tt < D / 32; ++tt) acc[tt] = f32x16{};
-    // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave) for tile u, A
-    // operands by transpose reads of the dO or Q tile.
-    auto accumulate = [&](int u) __attribute__((always_inline)) {
-        const unsigned char* tb = pwave ? dobuf[u % 3] : qbuf[u % 3];
+    // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave) for the tile in
+    // slot sl, A operands by transpose reads of the dO or Q tile.
+    auto accumulate = [&](auto role, int sl) __attribute__((always_inline)) {
+        const unsigned char* tb = decltype(role)::value ? dobuf[sl] : qbuf[sl];
 #pragma unroll
         for (int tt = 0; tt < D / 32; ++tt)
 #pragma unroll
@@ -307,54 +317,127 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                 for (int h2 = 0; h2 < 2; ++h2) {
                     const int base = (st * 32 + h2 * 16) * TL::kRowBytes;
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(tb + base + t_off[tt][0]));
+                        (lds_s16x4*)(tb + base + (t_base[0] ^ (tt << 6))));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(tb + base + t_off[tt][1]));
+                        (lds_s16x4*)(tb + base + (t_base[1] ^ (tt << 6))));
                     const s16x4 pair[2] = {lo, hi};
                     bf16x8 a;
                     __builtin_memcpy(&a, pair, sizeof(a));
                     acc[tt] = mfma(a, pf[st][h2], acc[tt]);
                 }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kDkdvReadAhead, 0);
+#pragma unroll
+        for (int i = 0; i < D / 32 * kBc / 16 - kDkdvReadAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kDkdvReadAhead, 0);
     };
 
-    // Prologue: tiles t0 and t0 + 1 resident, then S/P or dP of tile t0.
-    load_tile(t0);
-    if (t0 + 1 < nqt) load_tile(t0 + 1);
-    put_stats(t0, fetch_stats(t0));
-    if (t0 + 1 < nqt) put_stats(t0 + 1, fetch_stats(t0 + 1));
+    // Prologue: tiles t0 and t0 + 1 resident (slots 0 and 1), then P(t0)
+    // (P-wave) or dP(t0) (dS-wave).
+    load_tile(t0, 0);
+    if (t0 + 1 < nqt) load_tile(t0 + 1, 1);
+    put_stats(0, fetch_stats(t0));
+    if (t0 + 1 < nqt) put_stats(1, fetch_stats(t0 + 1));
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-    clear_tails(t0);
-    if (t0 + 1 < nqt) clear_tails(t0 + 1);
+    clear_tails(t0, 0);
+    if (t0 + 1 < nqt) clear_tails(t0 + 1, 1);
     __syncthreads();
-    scores(t0);
-    if (pwave) probs(t0);
-
-    // Step t: the dS-wave forms dS(t); both accumulate tile t (dV or dK);
-    // both form the scores of tile t + 1 (S or dP) and the P-wave P(t+1).
-    for (int t = t0; t < nqt; ++t) {
-        // P(t) and tile t + 1 are visible after this barrier; tile t - 1's
-        // buffers and P(t - 1) are no longer read.
-        __syncthreads();
-        float next_stats = 0.f;
-        if (!pwave) dscores(t);
-        // Tile t+2's loads after dS(t), so that the P-wave's first dV MFMAs
-        // and the dS-wave's VALU work do not queue behind them (1% faster
-        // than issuing them at the start of the step).
-        if (t + 2 < nqt) {
-            load_tile(t + 2);
-            next_stats = fetch_stats(t + 2);
-        }
-        accumulate(t);
-        if (t + 1 < nqt) {
-            scores(t + 1);
-            if (pwave) probs(t + 1);
-        }
-        if (t + 2 < nqt) {
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // this wave's loads of tile t+2
-            clear_tails(t + 2);
-            put_stats(t + 2, next_stats);
-        }
+    if (pwave) {
+        scores(std::true_type{}, 0);
+        probs(t0, 0, std::false_type{});
+    } else {
+        scores(std::false_type{}, 0);
     }
+
+    // Step t, two phases per SIMD pair:
+    //  phase 1: the P-wave runs dV(t) and S(t+1) on the matrix core while
+    //           the dS-wave forms dS(t) and issues tile t+2's loads;
+    //  phase 2: the dS-wave runs dK(t) and dP(t+1) while the P-wave issues
+    //           its share of tile t+2 and forms P(t+1).
+    // The phase barrier also orders P(t)'s reads before P(t+1)'s writes, so
+    // one P buffer suffices; the step barrier publishes P(t+1) and tile t+2.
+    // Each role runs its own copy of the loop. Steps whose tiles t+1 needs
+    // no causal mask and lies inside N, with t + 2 < nqt, are straight-line
+    // code, unrolled three at a time so that their slots are constants; the
+    // values that cross a barrier there pass through empty volatile asm on
+    // both sides of it, so the compiler keeps each phase's work in its phase.
+    // Values crossing the step barrier: the accumulator and P(t+1) (P-wave)
+    // or dP(t+1) (dS-wave); the phase barrier: the accumulator and S(t+1)
+    // (P-wave) or dS(t) (dS-wave).
+    auto pin = [&](auto role, auto mid) __attribute__((always_inline)) {
+        auto& pfr = pf;  // named outside the discarded branch so both are captured
+        auto& xr = x;
+#pragma unroll
+        for (int tt = 0; tt < D / 32; ++tt) asm volatile("" : "+v"(acc[tt]));
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) {
+            if constexpr (decltype(role)::value != decltype(mid)::value)
+                asm volatile("" : "+v"(pfr[st][0]), "+v"(pfr[st][1]));
+            else
+                asm volatile("" : "+v"(xr[st]));
+        }
+    };
+    // First step whose tile t + 1 needs no causal mask for any key of the block.
+    const int t_nomask = CAUSAL ? (k0 + kBwdRows - 1 + kBc - 1) / kBc - 1 : 0;
+    const int t_full_end = min(N / kBc - 1, nqt - 2);  // straight-line steps t < t_full_end
+    auto run = [&](auto role) __attribute__((always_inline)) {
+        constexpr bool PW = decltype(role)::value;
+        auto step = [&](auto full, int t, auto slot) __attribute__((always_inline)) {
+            constexpr bool FULL = decltype(full)::value;
+            const int s0 = slot;
+            const int s1 = s0 == 2 ? 0 : s0 + 1;
+            const int s2 = s0 == 0 ? 2 : s0 - 1;
+            if constexpr (FULL) pin(role, std::false_type{});
+            __syncthreads();
+            if constexpr (FULL) pin(role, std::false_type{});
+            float next_stats = 0.f;
+            if constexpr (PW) {
+                accumulate(role, s0);
+                if (FULL || t + 1 < nqt) scores(role, s1);
+            } else {
+                dscores(s0);
+                if (FULL || t + 2 < nqt) {
+                    load_tile(t + 2, s2);
+                    next_stats = fetch_stats(t + 2);
+                }
+            }
+            if constexpr (FULL) pin(role, std::true_type{});
+            __syncthreads();
+            if constexpr (FULL) pin(role, std::true_type{});
+            if constexpr (PW) {
+                if (FULL || t + 2 < nqt) {
+                    load_tile(t + 2, s2);
+                    next_stats = fetch_stats(t + 2);
+                }
+                if (FULL || t + 1 < nqt) probs(t + 1, s1, full);
+            } else {
+                accumulate(role, s0);
+                if (FULL || t + 1 < nqt) scores(role, s1);
+            }
+            if (FULL || t + 2 < nqt) {
+                __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // this wave's loads of tile t+2
+                clear_tails(t + 2, s2);
+                put_stats(s2, next_stats);
+            }
+        };
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        using C2 = std::integral_constant<int, 2>;
+        int t = t0, sl = 0;
+        // General steps up to the straight-line range, and on until slot 0.
+        for (; t < nqt && (t < t_nomask || sl != 0); ++t, sl = sl == 2 ? 0 : sl + 1)
+            step(std::false_type{}, t, sl);
+        for (; t + 3 <= t_full_end; t += 3) {
+            step(std::true_type{}, t, C0{});
+            step(std::true_type{}, t + 1, C1{});
+            step(std::true_type{}, t + 2, C2{});
+        }
+        for (; t < nqt; ++t, sl = sl == 2 ? 0 : sl + 1) step(std::false_type{}, t, sl);
+    };
+    if (pwave) run(std::true_type{});
+    else run(std::false_type{});
 
     if (kj < N) {
         if (pwave) store_row<D>(dv + head_off + (size_t)kj * D, acc, 1.0f, lh);

@@ -4,7 +4,7 @@
 // [FlashAttention: The GPU Memory Hack That Changed Everything
 //  (ai.branddocks.com, episode 75), "Standard Attention": S = QK^T is written
 //  to HBM, read back for softmax, P is written and read back for PV; "The
-//  Problem: Memory Bandwidth": those N x N round trips dominate.]
+//  Problem: GPU Memory Hierarchy": those N x N round trips dominate.]
 //
 // Steps 1 and 3 are plain batched GEMMs and go to rocBLAS (bf16 inputs, fp32
 // accumulation). Step 2, the row softmax over the stored scores, is this
