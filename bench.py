@@ -374,6 +374,152 @@ def bench_decode(args):
     return 0
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_time(w, q, k, v, budget_s: float):
+    """Wall time of the oracle on the whole workload: timed head by head until
+    budget_s, then extrapolated by useful FLOPs. longctx32k (whose parity test
+    samples rows) is timed on 256 sampled query rows per head the same way.
+    Returns (seconds for the whole config, description)."""
+    import oracle
+    from io_aware_tiled_09_amd.inputs import sample_rows, useful_flops
+    B, H, N, d = q.shape
+    total = useful_flops(B, H, N, d, w.causal)
+    done_flops, elapsed, heads = 0.0, 0.0, 0
+    rows_mode = w.name == "longctx32k"
+    while heads < B * H and (heads == 0 or elapsed < budget_s):
+        b, h = divmod(heads, H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t0 = time.perf_counter()
+        if rows_mode:
+            r = sample_rows(N, 256, seed=77 + heads)
+            oracle.attention_rows(q[sl], k[sl], v[sl], w.scale, w.causal, r)
+            vis = (r + 1).double() if w.causal else torch_full(r, N)
+            done_flops += float(4.0 * d * vis.sum())
+        else:
+            oracle.attention_fwd(q[sl], k[sl], v[sl], w.scale, w.causal)
+            done_flops += useful_flops(1, 1, N, d, w.causal)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+    whole = elapsed * total / done_flops
+    what = (f"{heads} of {B * H} heads" + (" x 256 sampled rows" if rows_mode else "")
+            + f" in {elapsed:.2f} s" + ("" if done_flops >= total else ", extrapolated by FLOPs"))
+    return whole, what
+
+
+def torch_full(r, N):
+    import torch
+    return torch.full(r.shape, float(N), dtype=torch.float64)
+
+
+def bench_table(args):
+    """Every configuration of the forward: GPU time per call and TFLOP/s, the
+    launch shape, and the oracle's wall time for the same config."""
+    import torch
+    import io_aware_tiled_09_amd as fa
+    import oracle
+    from io_aware_tiled_09_amd.inputs import WORKLOADS, make_qkv, useful_flops
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 3
+    fa.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cpu = cpu_model()
+    threads = oracle.num_threads()
+    rows = []
+    for name in ("single_head", "bert512", "gpt2_1k", "gpt2_1k_spiky", "longdoc8k", "longctx32k"):
+        w = WORKLOADS[name]
+        q, k, v = make_qkv(w)
+        dq, dk, dv = (t.to(dev) for t in (q, k, v))
+        o = torch.empty_like(dq)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+
+        def step(on=None):
+            st = fn(dq, dk, dv, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, on or stream)
+            if st != 0:
+                raise fa.FAError(st)
+        for _ in range(args.warmup):
+            step()
+        K = args.steps
+        flops = useful_flops(w.B, w.H, w.N, w.d, w.causal)
+
+        def median_of_5(run):
+            reps = []
+            for _ in range(5):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                run()
+                e1.record(stream)
+                e1.synchronize()
+                reps.append(e0.elapsed_time(e1) / K)
+            return sorted(reps)[2]
+
+        # (1) K calls back to back between two events: the host enqueues as
+        # fast as it can, and for kernels of a few microseconds the GPU may
+        # wait on it between calls.
+        stream_ms = median_of_5(lambda: [step() for _ in range(K)])
+        # (2) the same K calls captured once in a HIP graph and replayed: the
+        # device time per call without host launch gaps.
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(K):
+                    step(cap)
+        torch.cuda.synchronize()
+        graph_ms = median_of_5(g.replay)
+        del g
+        best_ms = min(stream_ms, graph_ms)
+        if w.dtype == "bf16":
+            grid, rows_per_block, paired = fa.fa_fwd_grid(w.B, w.H, w.N, w.causal)
+            shape = f"{grid} WGs x {rows_per_block} rows" + (", paired" if paired else "")
+            peak = PEAK_BF16_TFLOPS
+        else:
+            grid = w.B * w.H * ((w.N + 127) // 128)
+            shape = f"{grid} WGs x 128 rows (fp32 kernel: 3 bf16 MFMAs per product)"
+            peak = round(PEAK_BF16_TFLOPS / 3, 1)
+        ora_s, ora_what = oracle_time(w, q, k, v, args.cpu_budget if args.cpu_budget > 0 else 15.0)
+        row = {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+               "dtype": w.dtype, "launch": shape,
+               "us_stream": round(stream_ms * 1e3, 2), "us_graph": round(graph_ms * 1e3, 2),
+               "tflops": round(flops / (best_ms * 1e-3) / 1e12, 1),
+               "pct_of_peak": round(100.0 * flops / (best_ms * 1e-3) / 1e12 / peak, 2),
+               "peak": peak, "oracle_s": round(ora_s, 3), "oracle_timed": ora_what,
+               "oracle_over_gpu": round(ora_s / (best_ms * 1e-3), 0)}
+        log(f"{name}: {row['us_stream']} us/call in a stream, {row['us_graph']} us in a graph, "
+            f"{row['tflops']} TFLOP/s ({shape}); oracle {ora_s:.2f} s ({ora_what})")
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+        del dq, dk, dv, o, lse
+    print("| config | shape | launch | us / call, stream | us / call, graph | TFLOP/s | "
+          "% of peak | oracle wall | oracle / GPU |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['workload']} | B{r['B']} H{r['H']} N{r['N']} d{r['d']} "
+              f"{'causal' if r['causal'] else 'full'} {r['dtype']} | {r['launch']} | "
+              f"{r['us_stream']} | {r['us_graph']} | {r['tflops']} | {r['pct_of_peak']} | "
+              f"{r['oracle_s']} s ({r['oracle_timed']}) | {int(r['oracle_over_gpu'])}x |")
+    print(f"\nOracle: {threads} threads on {cpu} (model name from /proc/cpuinfo); TFLOP/s "
+          f"and % of peak from the faster of the two timings; useful FLOPs = 4 N^2 d B H "
+          f"(halved when causal).")
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,6 +549,11 @@ def main(argv=None):
                          "counter CSVs of a run made with --copy-kernel-mib")
     ap.add_argument("--profile-command", default="",
                     help="with --ingest-counters: the command line the counters came from")
+    ap.add_argument("--table", action="store_true",
+                    help="every forward configuration (single_head .. longctx32k): GPU time "
+                         "per call, TFLOP/s, launch shape and the oracle's wall time for the "
+                         "same config (--cpu-budget seconds per config, then extrapolated), "
+                         "one JSON line each and a markdown table")
     args = ap.parse_args(argv)
     if args.ingest_counters:
         return ingest_counters(*args.ingest_counters, args.copy_kernel_mib or 1024,
@@ -416,6 +567,8 @@ def main(argv=None):
 
     if args.pass_ == "decode":
         return bench_decode(args)
+    if args.table:
+        return bench_table(args)
 
     import torch
     import io_aware_tiled_09_amd as fa

@@ -183,11 +183,28 @@ int fa_decode_paged(const void *q, const void *k_cache, const void *v_cache,
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_string(int status);
 
-/* Queries per workgroup tile (Br) of the bf16 kernel (fa_fwd; fa_fwd_f32
+/* Queries per workgroup tile (Br) of the bf16 kernel on grids that fill the
+ * CUs (fa_fwd; smaller grids use 128-row blocks, see fa_fwd_grid; fa_fwd_f32
  * uses 128) and keys per K/V tile (Bc) of both kernels; informational, for
  * grid-size arithmetic in callers and tests. */
 int fa_tile_rows(void);
 int fa_tile_cols(void);
+
+/* Launch shape of fa_fwd for (B, H, N, causal): host arithmetic only, no GPU
+ * work, the same rule fa_fwd applies. The split over (batch*head x query
+ * block) follows [FlashAttention: The GPU Memory Hack That Changed
+ * Everything, "FlashAttention-2"] (parallelism over the sequence). Returns
+ * the number of workgroups fa_fwd launches: 0 for an empty shape,
+ * -FA_ERR_BAD_SHAPE for a negative size, -FA_ERR_TOO_LARGE past the grid
+ * limit. Where non-NULL, *rows_per_block receives the query rows of one
+ * block (256; 128 when a grid of 256-row blocks would leave CUs idle and the
+ * 128-row grid fits one workgroup per CU: the workgroup's two wave groups
+ * then take alternate key tiles of the block and merge their partial
+ * (max, sum, output) states with the two correction factors of [Flash
+ * Attention Optimization, "The fix: tile the computation..."]) and *paired
+ * whether causal blocks run two per workgroup. For callers that size work
+ * around the forward's grid, and for tests. */
+long long fa_fwd_grid(int B, int H, int N, int causal, int *rows_per_block, int *paired);
 
 #ifdef __cplusplus
 }

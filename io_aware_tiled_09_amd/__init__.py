@@ -12,10 +12,11 @@ from ._binding import (EXPORTS, FA_OK, FAError, LIB_PATH, attention, attention_b
                        attention_fp8, decode_paged, fa_bwd, fa_bwd_noalloc,
                        fa_bwd_noalloc_max_rows, fa_decode_paged,
                        fa_decode_workspace_bytes, fa_fwd, fa_fwd_f32, fa_fwd_fp8,
-                       fa_status_string, fa_tile_cols, fa_tile_rows, load)
+                       fa_fwd_grid, fa_status_string, fa_tile_cols, fa_tile_rows, load)
 
 __all__ = ["attention", "attention_backward", "attention_fp8", "decode_paged", "fa_fwd",
            "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows",
            "fa_decode_paged", "fa_decode_workspace_bytes",
-           "fa_status_string", "fa_tile_rows", "fa_tile_cols", "FAError", "FA_OK", "EXPORTS",
+           "fa_status_string", "fa_tile_rows", "fa_tile_cols", "fa_fwd_grid", "FAError", "FA_OK",
+           "EXPORTS",
            "LIB_PATH", "load"]

@@ -24,7 +24,7 @@ STATUS_NAMES = {
 }
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc",
            "fa_bwd_noalloc_max_rows", "fa_decode_paged", "fa_decode_workspace_bytes",
-           "fa_status_string", "fa_tile_rows", "fa_tile_cols")
+           "fa_status_string", "fa_tile_rows", "fa_tile_cols", "fa_fwd_grid")
 
 
 class FAError(RuntimeError):
@@ -63,6 +63,8 @@ def load():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_tile_rows.restype = i
     lib.fa_tile_cols.restype = i
+    lib.fa_fwd_grid.argtypes = [i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.fa_fwd_grid.restype = ctypes.c_longlong
     _lib = lib
     return lib
 
@@ -161,6 +163,17 @@ def fa_tile_rows() -> int:
 
 def fa_tile_cols() -> int:
     return int(load().fa_tile_cols())
+
+
+def fa_fwd_grid(B: int, H: int, N: int, causal: bool):
+    """fa_fwd's launch shape: (workgroups, query rows per block, paired).
+    Raises FAError for invalid sizes."""
+    rows, paired = ctypes.c_int(0), ctypes.c_int(0)
+    g = int(load().fa_fwd_grid(int(B), int(H), int(N), int(bool(causal)),
+                               ctypes.byref(rows), ctypes.byref(paired)))
+    if g < 0:
+        raise FAError(-g)
+    return g, rows.value, bool(paired.value)
 
 
 def _need(t, name, shape, dtype, device):

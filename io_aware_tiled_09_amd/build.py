@@ -18,6 +18,7 @@ SOURCES = [os.path.join(PKG, "csrc", "fa_fwd_bf16.hip"),
            os.path.join(PKG, "csrc", "fa_fwd_fp8.hip"),
            os.path.join(PKG, "csrc", "fa_decode.hip"),
            os.path.join(PKG, "csrc", "fa_scratch.hip"),
+           os.path.join(PKG, "csrc", "fa_plan.cpp"),
            os.path.join(PKG, "csrc", "fa_api.cpp")]
 ARCH = "gfx950"
 

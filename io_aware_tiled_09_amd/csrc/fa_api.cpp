@@ -311,4 +311,22 @@ const char* fa_status_string(int status)
 int fa_tile_rows(void) { return fa::kBrBf16; }
 int fa_tile_cols(void) { return fa::kBc; }
 
+long long fa_fwd_grid(int B, int H, int N, int causal, int* rows_per_block, int* paired)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return -FA_ERR_BAD_SHAPE;
+    if (B == 0 || H == 0 || N == 0) {
+        if (rows_per_block) *rows_per_block = fa::kBrBf16;
+        if (paired) *paired = 0;
+        return 0;
+    }
+    const long long nqb = ((long long)N + fa::kBr - 1) / fa::kBr;
+    if ((long long)B * H * nqb > 0x7fffffffLL)
+        return -FA_ERR_TOO_LARGE;
+    const fa::FwdPlan pl = fa::fwd_plan((long long)B * H, N, causal != 0);
+    if (rows_per_block) *rows_per_block = pl.rows;
+    if (paired) *paired = pl.paired ? 1 : 0;
+    return pl.grid;
+}
+
 }  // extern "C"

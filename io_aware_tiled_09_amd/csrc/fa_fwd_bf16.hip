@@ -90,12 +90,19 @@ constexpr int kReadAhead = 6;
 constexpr float kMaxSlack = 3.0f;
 static_assert(kBrBf16 == kPPWaves * 32, "32 query rows per wave");
 
-template <int D, bool CAUSAL, bool PAIRED>
+// KS = 1: each workgroup covers 256 query rows and both wave groups see every
+// key tile. KS = 2 (grids too small to fill the CUs): a workgroup covers 128
+// rows, waves w and w + 4 own the same 32 rows, group g takes the key tiles
+// t = g (mod 2), and the two partial (max, sum, output) states of a row are
+// merged at the end with two correction factors.
+template <int D, bool CAUSAL, bool PAIRED, int KS>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                         const __bf16* __restrict__ v, __bf16* __restrict__ o,
                         float* __restrict__ lse, int BH, int N, int nqb, float scale_log2)
 {
+    static_assert(KS == 1 || (KS == 2 && !PAIRED), "key split only for one block per workgroup");
+    constexpr int kRowsWG = kBrBf16 / KS;  // query rows per workgroup
     using TL = Tile<D, kPPWaves>;
     constexpr int L = TL::kLoadsPerWave;
     // Tile t of K lives in kring[t % 4], tile t of V in vring[t % 4]; rows
@@ -106,6 +113,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases in SGPRs
     const int grp = wave >> 2;  // waves w and w+4 share a SIMD
+    const int wq = KS == 1 ? wave : (wave & 3);  // the wave's 32-row slot in the block
     const int lane = tid & 63;
     const int li = lane & 31;   // query column of this lane in the wave's 32
     const int lh = lane >> 5;   // which 8-element half of each 16-wide k slice
@@ -131,8 +139,8 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     const __bf16* kh = k + head_off;
     const __bf16* vh = v + head_off;
 
-    const int q0 = qb * kBrBf16;
-    const int qw0 = q0 + wave * 32;   // first query of this wave
+    const int q0 = qb * kRowsWG;
+    const int qw0 = q0 + wq * 32;     // first query of this wave
     const int qi = qw0 + li;          // this lane's query row
 
     // Q fragment (B operand of S^T = K Q^T): row qi, d slice c*16 + lh*8 + 0..7.
@@ -147,7 +155,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
     const int nkb_all = (N + kBc - 1) / kBc;
-    const int nkb = CAUSAL ? min(nkb_all, (q0 + kBrBf16 - 1) / kBc + 1) : nkb_all;
+    const int nkb = CAUSAL ? min(nkb_all, (q0 + kRowsWG - 1) / kBc + 1) : nkb_all;
     // Last tile with a key visible to some row of this wave.
     const int last = CAUSAL ? min(nkb - 1, (qw0 + 31) / kBc) : nkb - 1;
 
@@ -299,8 +307,8 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     if (nkb <= 2) clear_tail(nkb - 1, vring[nkb - 1]);
     __syncthreads();
     f32x16 sc[kBc / 32];  // scores of the tile whose softmax runs next
-    scores(0, sc);
-    __syncthreads();  // every wave is done with K_0 before K_4 replaces it
+    scores(KS == 1 ? 0 : grp, sc);  // KS = 2: group g starts with tile g
+    __syncthreads();  // every wave is done with K_0 (K_1) before K_4 (K_5) replaces it
 
     // Phases. Global phase s: group 0 runs A(s/2) for even s and B(s/2) for
     // odd s; group 1 runs one phase later. A(j) is VALU work only (softmax of
@@ -316,8 +324,20 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // may still be in flight, those of phase s-4 have landed, and the
     // barrier publishes them. K_t is first read in phase 2t-1, V_t in phase
     // 2t+1.
+    // KS = 2: tiles are consumed twice as fast (K_t is read in phase t - 1 and
+    // V_t in phase t + 1, by group t % 2), so every phase loads one K and one
+    // V tile: K_{s+4} into the slot of K_s (last read in phase s - 1) and
+    // V_{s+2} into the slot of V_{s-2} (last read in phase s - 1), both first
+    // read in phase s + 3. The loading group issues 4L loads per wave every
+    // other phase, so the same vmcnt(4L) at every phase end leaves only the
+    // current phase's loads in flight and publishes those of phase s - 2.
     auto phase_loads = [&](int s) __attribute__((always_inline)) {
         if ((s & 1) != grp) return;
+        if constexpr (KS == 2) {
+            issue_grp(kh, s + 4, kring[(s + 4) & 3]);
+            issue_grp(vh, s + 2, vring[(s + 2) & 3]);
+            return;
+        }
         if ((s & 1) == 0) {
             const int t = s / 2 + 2;
             issue_grp(vh, t, vring[t & 3]);
@@ -332,7 +352,9 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // loading group's waits cover it). The scheduling fences keep every
     // instruction inside its phase: the compiler would otherwise move MFMAs
     // and VALU work across the barrier and break the pairing of the groups.
-    const int tail_phase = (nkb > 2 && N % kBc != 0 && nkb == nkb_all) ? 2 * nkb - 2 : -1;
+    // (KS = 2: V_{nkb-1} is issued in phase nkb - 3, read in phase nkb.)
+    const int tail_phase = (nkb > 2 && N % kBc != 0 && nkb == nkb_all)
+                               ? (KS == 1 ? 2 * nkb - 2 : nkb - 1) : -1;
     auto phase_end = [&](int s) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * L));
@@ -424,7 +446,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     auto phase_b = [&](auto full, int kb, int kslot, int vslot) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full)::value;
         if constexpr (PAIRED) asm volatile("" : "+v"(k_off[0]), "+v"(v_off[0][0]), "+v"(v_off[0][1]));
-        if (FULL || kb + 1 <= last) {
+        if (FULL || kb + KS <= last) {  // the wave's next tile is kb + KS
             scores(kslot, sc);
             // K fragments kReadAhead MFMAs ahead, no further (VGPR budget).
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadAhead, 0);
@@ -528,6 +550,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         phase_loads(0);
         phase_end(0);
     }
+    if constexpr (KS == 1) {
     // Steps j < kb_full are full; kb_full <= nkb - 2 keeps the phase of the
     // partial tile's clear (2 nkb - 2, which group 1 reaches in step nkb - 2)
     // in the general path for both groups, so both meet its extra barrier.
@@ -547,6 +570,21 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         step(std::integral_constant<int, 2>{}, kb + 2);
         step(std::integral_constant<int, 3>{}, kb + 3);
     }
+    } else {
+    // KS = 2: step j of group g is tile t = 2j + g, with A(t) in phase t and
+    // B(t) (scores of tile t + 2, then P_t V_t) in phase t + 1. Both groups
+    // run ceil(nkb / 2) steps; a group past its last tile only issues its
+    // (empty) loads and meets the barriers.
+    for (int j = 0; 2 * j < nkb; ++j) {
+        const int t = 2 * j + grp;
+        phase_loads(t);
+        phase_a(std::false_type{}, t);
+        phase_end(t);
+        phase_loads(t + 1);
+        phase_b(std::false_type{}, t, (t + 2) & 3, t & 3);
+        phase_end(t + 1);
+    }
+    }
     // ---- epilogue: O = acc / l, lse = (m2 + log2 l) * ln 2
     auto epilogue = [&]() __attribute__((always_inline)) {
     const float l_tot = sum_with_partner(l_run);
@@ -563,6 +601,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
     }
     };
+    if constexpr (KS == 1) {
     // Group 0's outputs are final after its last MFMA phase: it stores them in
     // the phase in which group 1 runs its last MFMA phase (no tile is loaded
     // or read by group 0 there any more), then meets that phase's barrier.
@@ -574,38 +613,72 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // No load may still be landing in LDS when the workgroup ends.
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     if (grp == 1) epilogue();
+    } else {
+    // KS = 2: group 0 meets the barrier of group 1's last phase; then, with
+    // every load landed and every ring read done, group 1 hands its (m, l,
+    // acc) to group 0 through the K ring (lane-major 16-byte slots) and the
+    // V ring, and group 0 merges the two states of each row with the factors
+    // 2^(m_g - m), m = max(m_0, m_1), and stores the rows.
+    if (grp == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __syncthreads();
+    static_assert(kPPWaves / 2 * (D / 32) * 4 * 64 * 16 <= kRing * TL::kBytes, "exchange fits the K ring");
+    float* xm = reinterpret_cast<float*>(vring[0]);  // [wave slot][m, l][lane]
+    auto xacc = [&](int tt, int g) __attribute__((always_inline)) {
+        return reinterpret_cast<f32x4*>(kring[0] + (((wq * (D / 32) + tt) * 4 + g) * 64 + lane) * 16);
+    };
+    if (grp == 1) {
+        xm[(wq * 2 + 0) * 64 + lane] = m_run;
+        xm[(wq * 2 + 1) * 64 + lane] = l_run;
+#pragma unroll
+        for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *xacc(tt, g) = f32x4{acc[tt][g * 4 + 0], acc[tt][g * 4 + 1], acc[tt][g * 4 + 2],
+                                     acc[tt][g * 4 + 3]};
+    }
+    __syncthreads();
+    if (grp == 0) {
+        const float m1 = xm[(wq * 2 + 0) * 64 + lane];
+        const float l1 = xm[(wq * 2 + 1) * 64 + lane];
+        const float m = fmaxf(m_run, m1);
+        // a group that saw no visible key of the row has m = -inf, l = 0, acc = 0
+        const float a0 = m_run > neg_inf() ? __builtin_amdgcn_exp2f(m_run - m) : 0.f;
+        const float a1 = m1 > neg_inf() ? __builtin_amdgcn_exp2f(m1 - m) : 0.f;
+        l_run = l_run * a0 + l1 * a1;
+        m_run = m;
+#pragma unroll
+        for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 x = *xacc(tt, g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[tt][g * 4 + i] = acc[tt][g * 4 + i] * a0 + x[i] * a1;
+            }
+        epilogue();
+    }
+    }
     }  // work items
 }
-
-// Causal grids run one workgroup per pair of query blocks (the i-th
-// heaviest with the i-th lightest) when the grid is small or N <= 8192: with
-// one block each, the heavy blocks (many key tiles) and the light ones land
-// unevenly on the CUs. The paired kernel measured 1-17% faster for d = 128
-// causal at N <= 8192 on grids of 1024-2048 blocks, and even at N = 16384,
-// so longer sequences keep one block per workgroup.
-constexpr long long kPairMaxGrid = 2 * 256;  // 256 CUs on MI355X
-constexpr int kPairMaxN = 8192;
 
 template <int D, bool CAUSAL>
 hipError_t launch_one(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
                       int BH, int N, float scale_log2, hipStream_t stream)
 {
-    const int nqb = (N + kBrBf16 - 1) / kBrBf16;
-    const long long blocks = (long long)BH * nqb;
-    const bool paired = nqb > 1 && (blocks <= kPairMaxGrid || N <= kPairMaxN);
-    if constexpr (CAUSAL) {
-        if (paired) {
-            const dim3 grid((unsigned)((long long)BH * ((nqb + 1) / 2)));
-            hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, true, true>), grid, dim3(kPPThreads), 0,
-                               stream, q, k, v, o, lse, BH, N, nqb, scale_log2);
-            return hipGetLastError();
-        }
-    }
-    {
-        const dim3 grid((unsigned)blocks);
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, false>), grid, dim3(kPPThreads), 0, stream,
-                           q, k, v, o, lse, BH, N, nqb, scale_log2);
-    }
+    const FwdPlan pl = fwd_plan(BH, N, CAUSAL);
+    const dim3 grid((unsigned)pl.grid);
+    if (pl.key_split == 2)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, false, 2>), grid, dim3(kPPThreads), 0,
+                           stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
+    else if (CAUSAL && pl.paired)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, CAUSAL, 1>), grid, dim3(kPPThreads), 0,
+                           stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
+    else
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, false, 1>), grid, dim3(kPPThreads), 0,
+                           stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
     return hipGetLastError();
 }
 

@@ -14,6 +14,17 @@ constexpr int kBrBf16 = 256;         // query rows per workgroup of the bf16 ker
 // scale_log2 = softmax scale * log2(e) >= 0.
 hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                        int BH, int N, int d, float scale_log2, bool causal, hipStream_t stream);
+// Grid of the bf16 forward for a shape: rows per query block (256, or 128
+// when the two wave groups split the key range), whether causal blocks run
+// in pairs, and the number of workgroups.
+struct FwdPlan {
+    int key_split;      // 1 or 2
+    bool paired;
+    int rows;           // query rows per block
+    int nqb;            // query blocks per head
+    long long grid;     // workgroups
+};
+FwdPlan fwd_plan(long long BH, int N, bool causal);
 hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                       int BH, int N, int d, float scale_log2, bool causal, hipStream_t stream);
 // Backward pass (bf16 tensors, fp32 lse); delta: BH*N floats of workspace.

@@ -80,11 +80,12 @@ __device__ inline unsigned lds_addr(const void* p) {
 // `voff` of the buffer land at LDS address base + 16*i. Issued as inline asm
 // so that the compiler's wait-count pass does not treat later LDS reads of
 // other buffers as dependent on it; kernels wait for these loads explicitly
-// (vmcnt) before the barrier that publishes a tile. M0 carries the LDS base;
-// the kernels use M0 for nothing else.
+// (vmcnt) before the barrier that publishes a tile. The LDS base goes in
+// M0 as an input operand of the asm ("{m0}"), so the compiler itself sets M0
+// and knows what it holds.
 __device__ inline void lds_dma16(i32x4 rsrc, unsigned voff, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(lds_base), "s"(rsrc) : "memory");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "{m0}"(lds_base) : "memory");
 }
 
 }  // namespace fa

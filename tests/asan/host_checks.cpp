@@ -78,6 +78,19 @@ int main()
     EXPECT(fa_decode_paged(P(0), P(64 * MB), P(128 * MB), I(192 * MB), I(193 * MB), P(194 * MB), F(195 * MB), P(196 * MB), ws, 3, 8, 2, 128, 40, 16, 10, 0.1f, nullptr), FA_OK, 1);
     EXPECT(fa_decode_paged(P(0), P(64 * MB), P(128 * MB), I(192 * MB), I(193 * MB), P(194 * MB), F(195 * MB), P(196 * MB), ws - 1, 3, 8, 2, 128, 40, 16, 10, 0.1f, nullptr), FA_ERR_WORKSPACE, 0);
     EXPECT(fa_decode_paged(P(0), P(64 * MB), P(128 * MB), I(192 * MB), I(193 * MB), P(194 * MB), F(195 * MB), P(196 * MB), ws, 3, 8, 3, 128, 40, 16, 10, 0.1f, nullptr), FA_ERR_BAD_SHAPE, 0);
+    // launch shape (host arithmetic only)
+    {
+        int rows = 0, paired = 0;
+        const long long g1 = fa_fwd_grid(4, 12, 512, 0, &rows, &paired);
+        const long long g2 = fa_fwd_grid(2, 32, 8192, 1, &rows, &paired);
+        const long long g3 = fa_fwd_grid(1 << 16, 1 << 14, 1 << 20, 0, nullptr, nullptr);
+        const long long g4 = fa_fwd_grid(-1, 2, 3, 1, nullptr, nullptr);
+        if (g1 != 192 || g2 != 1024 || rows != 256 || paired != 1 || g3 != -FA_ERR_TOO_LARGE ||
+            g4 != -FA_ERR_BAD_SHAPE) {
+            printf("FAIL: fa_fwd_grid %lld %lld %lld %lld\n", g1, g2, g3, g4);
+            ++g_fail;
+        }
+    }
     // every status has a description
     for (int s = 0; s <= 11; ++s)
         if (!fa_status_string(s) || !fa_status_string(s)[0]) { printf("FAIL: status %d\n", s); ++g_fail; }

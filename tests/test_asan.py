@@ -22,6 +22,7 @@ def test_argument_checks_under_asan(tmp_path):
            "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
            os.path.join(ROOT, "tests", "asan", "host_checks.cpp"),
            os.path.join(ROOT, "io_aware_tiled_09_amd", "csrc", "fa_api.cpp"),
+           os.path.join(ROOT, "io_aware_tiled_09_amd", "csrc", "fa_plan.cpp"),
            "-o", str(exe)]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",

@@ -43,6 +43,33 @@ def test_tile_shape():
     assert fa.fa_tile_rows() == 256 and fa.fa_tile_cols() == 64
 
 
+@pytest.mark.parametrize("B,H,N,causal,expect", [
+    # (workgroups, rows per block, paired)
+    (4, 12, 512, 0, (192, 128, False)),     # BERT shape: 96 blocks of 256 rows -> key split
+    (8, 12, 1024, 1, (192, 256, True)),     # GPT-2 shape: 768 key-split blocks would take 3 rounds
+    (2, 32, 8192, 1, (1024, 256, True)),    # long document: paired
+    (1, 32, 32768, 1, (4096, 256, False)),  # very long context: one block per workgroup
+    (1, 2, 65, 1, (2, 256, False)),         # one block either way: 256 rows
+    (1, 2, 200, 0, (4, 128, False)),
+    (1, 4, 8000, 1, (252, 128, False)),
+    (1, 16, 8000, 1, (256, 256, True)),
+    (2, 16, 1000, 0, (256, 128, False)),
+    (2, 16, 1100, 0, (160, 256, False)),   # 128-row grid (288) would not fit one round
+    (1, 1, 0, 0, (0, 256, False)),
+])
+def test_forward_grid(B, H, N, causal, expect):
+    assert fa.fa_fwd_grid(B, H, N, causal) == expect
+
+
+def test_forward_grid_errors():
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd_grid(-1, 2, 3, 0)
+    assert e.value.status == 2
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd_grid(1 << 16, 1 << 14, 1 << 20, 0)
+    assert e.value.status == 8
+
+
 def _call(fn=fa.fa_fwd, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
           B=1, H=2, N=100, d=64, scale=0.125, causal=0):
     return fn(q, k, v, o, lse, B, H, N, d, scale, causal, 0)

@@ -40,15 +40,62 @@ def test_ragged_multi_tile(d, causal):
     check_full(q, k, v, causal, 1.0 / math.sqrt(d), "N=333")
 
 
-@pytest.mark.parametrize("B,H,N,d", [(1, 3, 700, 64), (1, 3, 700, 128), (2, 2, 1300, 128),
-                                     (1, 2, 2100, 64), (3, 1, 513, 128)])
+def _grid(B, H, N, causal):
+    """fa_fwd's launch shape (workgroups, rows per block, paired)."""
+    return fa.fa_fwd_grid(B, H, N, causal)
+
+
+def _boundary_rows(N, *extra):
+    """Rows at block and tile edges (0, 63, 64, 127, 128, 255, 256, ...) and
+    the last rows, within [0, N)."""
+    rows = {0, 1, N - 2, N - 1, *extra}
+    for b in range(0, N + 256, 128):
+        rows.update({b - 1, b, b + 63, b + 64})
+    return sorted(r for r in rows if 0 <= r < N)
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 128, 700, 64), (1, 128, 700, 128), (2, 64, 1300, 128),
+                                     (1, 128, 2100, 64), (3, 64, 513, 128)])
 def test_paired_query_blocks(B, H, N, d):
-    # Causal grids with N <= 8192 run one workgroup per pair of query blocks
-    # (nqb-1-p, p); odd block counts leave the middle block alone and ragged
-    # N puts the partial block in a pair.
-    say(f"paired blocks B={B} H={H} N={N} d={d} causal")
+    # Causal grids with N <= 8192 that fill the CUs run one workgroup per pair
+    # of 256-row query blocks (nqb-1-p, p); odd block counts leave the middle
+    # block alone and ragged N puts the partial block in a pair. Many heads,
+    # so that the paired grid has at least 256 workgroups; rows sampled per
+    # head, every block and tile edge included.
+    grid, rows_per_block, paired = _grid(B, H, N, True)
+    assert rows_per_block == 256 and paired and grid >= 256
+    say(f"paired blocks B={B} H={H} N={N} d={d} causal ({grid} workgroups)")
     q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=N + d + B)
-    check_full(q, k, v, True, 1.0 / math.sqrt(d), f"paired N={N} d={d}")
+    edge = torch.tensor(_boundary_rows(N), dtype=torch.int64)
+    rows = torch.cat([sample_rows(N, 12, seed=N + d, heads=B * H), edge.expand(B * H, -1)], 1)
+    check_rows(q, k, v, True, 1.0 / math.sqrt(d), rows, f"paired N={N} d={d}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [129, 200, 257, 333, 700, 1000, 2100])
+def test_key_split_blocks(N, d, causal):
+    # Grids too small for the CUs run 128-row blocks whose two wave groups take
+    # alternate key tiles and merge their (max, sum, output) states: every
+    # output against the oracle, ragged tails and odd tile counts included.
+    grid, rows_per_block, paired = _grid(1, 2, N, causal)
+    assert rows_per_block == 128 and not paired
+    say(f"key split B=1 H=2 N={N} d={d} causal={causal} ({grid} workgroups)")
+    q, k, v = make_qkv(B=1, H=2, N=N, d=d, seed=N * 3 + d + causal)
+    check_full(q, k, v, causal, 1.0 / math.sqrt(d), f"key split N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_split_wide(d, causal):
+    # The largest key-split grids (256 workgroups) with long rows: B=2 H=16
+    # N=1000 (8 blocks of 128 per head).
+    B, H, N = 2, 16, 1000
+    grid, rows_per_block, _ = _grid(B, H, N, causal)
+    assert rows_per_block == 128 and grid == 256
+    say(f"key split wide B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=1000 + d + causal)
+    check_full(q, k, v, causal, 1.0 / math.sqrt(d), f"key split wide d={d} causal={causal}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -56,6 +103,7 @@ def test_unpaired_causal_ragged(d):
     # Past N = 8192 a causal grid of more than 512 query blocks runs one block
     # per workgroup; N = 8300 leaves a ragged last block of 108 rows.
     B, H, N = 1, 16, 8300
+    assert _grid(B, H, N, True) == (16 * 33, 256, False)
     say(f"unpaired causal B={B} H={H} N={N} d={d}")
     q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=8300 + d)
     rows = sample_rows(N, 24, seed=91 + d, heads=B * H)
@@ -66,17 +114,22 @@ def test_unpaired_causal_ragged(d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_paired_long_ragged(d):
-    # N = 8000 <= 8192: the paired kernel over 32 query blocks (16 pairs) per
-    # head, the last block ragged (64 rows) and paired with block 0.
-    B, H, N = 1, 4, 8000
-    say(f"paired long ragged B={B} H={H} N={N} d={d}")
-    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=8000 + d)
+@pytest.mark.parametrize("H", [16, 4])
+def test_long_ragged(H, d):
+    # N = 8000 <= 8192, causal. H = 16: the paired kernel over 32 query blocks
+    # (16 pairs) per head, the last block ragged (64 rows) and paired with
+    # block 0. H = 4: 252 key-split workgroups of 128 rows (63 per head), the
+    # last one ragged.
+    B, N = 1, 8000
+    grid, rows_per_block, paired = _grid(B, H, N, True)
+    assert (rows_per_block, paired) == ((256, True) if H == 16 else (128, False))
+    say(f"long ragged B={B} H={H} N={N} d={d} ({grid} workgroups of {rows_per_block} rows)")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=8000 + d + H)
     rows = sample_rows(N, 32, seed=57 + d, heads=B * H)
-    fixed = torch.tensor([0, 1, 255, 256, 3967, 3968, 4031, 7935, 7936, 7937, N - 2, N - 1],
-                         dtype=torch.int64)
+    fixed = torch.tensor([0, 1, 127, 128, 255, 256, 3967, 3968, 4031, 7935, 7936, 7937, N - 2,
+                          N - 1], dtype=torch.int64)
     check_rows(q, k, v, True, 1.0 / math.sqrt(d), torch.cat([rows, fixed.expand(B * H, -1)], 1),
-               f"paired long N={N} d={d}")
+               f"long ragged H={H} N={N} d={d}")
 
 
 def _random_shapes(n=12, seed=4242):
