@@ -155,3 +155,97 @@ def flash_fwd_fp8(q, k, v, scale, causal, tile=128, slack=3.0, pscale=48.0):
     o = bf16(acc * (F32(1.0) / l)[:, None])
     lse = ((m + np.log2(l / F32(pscale)).astype(F32)) * F32(LN2)).astype(F32)
     return o, lse
+
+
+def standard_rows(q, k, v, scale, causal, rows=None):
+    """The standard (materializing) path's rounding points for one head:
+    S = scale * (Q K^T) with fp32 accumulation of the exact bf16 products,
+    the row softmax in fp32 (max, p = exp2(s log2e - m log2e), sum, times
+    1/sum), P rounded to bf16, O = P V with fp32 accumulation, O rounded to
+    bf16; lse = m + log2(sum) ln 2. rows: query rows to model (default all).
+    Returns (o [R, d], lse [R]) float64."""
+    n = q.shape[0]
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    s = (q[rows].astype(F32) @ k.astype(F32).T).astype(F32) * F32(scale)
+    if causal:
+        s = np.where(np.arange(n)[None, :] <= rows[:, None], s, F32(-np.inf))
+    m = s.max(axis=1, keepdims=True)
+    mc = (m * F32(LOG2E)).astype(F32)
+    p = np.exp2(fma32(s, np.full_like(s, LOG2E), -np.broadcast_to(mc, s.shape)))
+    p = np.where(np.isneginf(s), F32(0), p).astype(F32)
+    l = p.sum(axis=1, dtype=F32, keepdims=True)
+    pb = bf16(p * (F32(1) / l))
+    o = bf16((pb @ v.astype(F32)).astype(F32))
+    lse = m[:, 0].astype(np.float64) + np.log2(l[:, 0].astype(np.float64)) * LN2
+    return o.astype(np.float64), lse
+
+
+def decode_row(q, k, v, c_log2, unroll):
+    """The decode kernels' rounding points for one (sequence, query head):
+    q [d], k, v [L, d] float32 holding bf16 values; c_log2 = float32(scale *
+    log2 e). Keys go in runs of 512; in a run, group g (of 16) takes key
+    16 b + g of each 16-key block b, `unroll` blocks at a time: the batch's
+    max moves the group's reference, l and acc are rescaled once, then each
+    key adds p = exp2(s - m) (fp32 dot products: each of 16 lanes sums its
+    d/16 slice with fmas, then a butterfly over the 16 lanes). The 16 group
+    states merge in pairs (g, g^1), then (g, g^2), then the four resulting
+    states in order; the runs merge in order; O = acc * (1/l) rounded to
+    bf16, lse = (m + log2 l) ln 2. Returns (o [d] float64, lse float)."""
+    L, d = k.shape
+    E = d // 16
+    # fp32 dot products in the kernel's order
+    qs = q.reshape(16, E).astype(F32)
+    ks = k.reshape(L, 16, E).astype(F32)
+    part = np.zeros((L, 16), dtype=F32)
+    for e in range(E):
+        part = fma32(np.broadcast_to(qs[:, e], (L, 16)), ks[:, :, e], part)
+    for off in (8, 4, 2, 1):
+        part = (part + part[:, np.arange(16) ^ off]).astype(F32)
+    s_all = (part[:, 0] * F32(c_log2)).astype(F32)
+
+    def merge(a, b):
+        m1, l1, a1 = a
+        m2, l2, a2 = b
+        mn = max(m1, m2)
+        if mn == -np.inf:
+            return a
+        f1 = np.exp2(F32(m1 - mn)).astype(F32)
+        f2 = np.exp2(F32(m2 - mn)).astype(F32)
+        return (mn, F32(F32(l1 * f1) + F32(l2 * f2)),
+                (a1 * f1 + a2 * f2).astype(F32))
+
+    runs = []
+    for r0 in range(0, L, 512):
+        r1 = min(L, r0 + 512)
+        groups = []
+        for g in range(16):
+            m, l, acc = -np.inf, F32(0), np.zeros(d, dtype=F32)
+            keys = list(range(r0 + g, r1, 16))
+            for b0 in range(0, (r1 - r0 + 15) // 16, unroll):
+                batch = [r0 + 16 * b + g for b in range(b0, b0 + unroll) if r0 + 16 * b + g < r1]
+                if not batch:
+                    continue
+                mx = max(float(s_all[j]) for j in batch)
+                mn = max(m, mx)
+                alpha = np.exp2(F32(m - mn)).astype(F32) if m != -np.inf else F32(0)
+                m = mn
+                l = F32(l * alpha)
+                acc = (acc * alpha).astype(F32)
+                for j in batch:
+                    p = np.exp2(F32(s_all[j] - F32(mn))).astype(F32)
+                    l = F32(l + p)
+                    acc = fma32(np.full(d, p, dtype=F32), v[j].astype(F32), acc)
+            del keys
+            groups.append((F32(m) if m != -np.inf else -np.inf, l, acc))
+        for off in (1, 2):
+            groups = [merge(groups[g], groups[g ^ off]) for g in range(16)]
+        st = groups[0]
+        for w in (4, 8, 12):
+            st = merge(st, groups[w])
+        runs.append(st)
+    st = runs[0]
+    for r in runs[1:]:
+        st = merge(st, r)
+    m, l, acc = st
+    o = bf16((acc * (F32(1) / l)).astype(F32))
+    return o.astype(np.float64), (float(m) + float(np.log2(np.float64(l)))) * LN2
