@@ -202,8 +202,10 @@ int fa_tile_cols(void);
  * then take alternate key tiles of the block and merge their partial
  * (max, sum, output) states with the two correction factors of [Flash
  * Attention Optimization, "The fix: tile the computation..."]) and *paired
- * whether causal blocks run two per workgroup. For callers that size work
- * around the forward's grid, and for tests. */
+ * whether causal blocks run two per workgroup (on small causal grids grouped
+ * so that every workgroup carries the heaviest block's work: {nqb-1},
+ * {nqb-2-p, p} and the middle blocks of two heads). For callers that size
+ * work around the forward's grid, and for tests. */
 long long fa_fwd_grid(int B, int H, int N, int causal, int *rows_per_block, int *paired);
 
 #ifdef __cplusplus

@@ -95,13 +95,59 @@ static_assert(kBrBf16 == kPPWaves * 32, "32 query rows per wave");
 // rows, waves w and w + 4 own the same 32 rows, group g takes the key tiles
 // t = g (mod 2), and the two partial (max, sum, output) states of a row are
 // merged at the end with two correction factors.
-template <int D, bool CAUSAL, bool PAIRED, int KS>
+// Items of workgroup L of the balanced causal grid (see fwd_plan): in
+// logical order, each head contributes {nqb-1} and {nqb-2-p, p} for
+// p < (nqb-1)/2, and for even nqb every two heads share one workgroup of
+// their middle blocks (nqb-2)/2, placed after the two heads' own; the
+// logical order is spread over the XCDs in contiguous runs, as block_coords
+// does. Heavier block first.
+__device__ inline void balanced_items(int L, int BH, int nqb, int& bh0, int& qb0, int& bh1,
+                                      int& qb1, int& nitems)
+{
+    const int per = 1 + (nqb - 1) / 2;
+    const bool mid = nqb % 2 == 0;
+    const int total = BH * per + (mid ? (BH + 1) / 2 : 0);
+    const int idx = total % kXcds == 0 ? (L % kXcds) * (total / kXcds) + L / kXcds : L;
+    const int grp_sz = mid ? 2 * per + 1 : per;       // WGs per head pair (even nqb) or head
+    const int g = idx / grp_sz, r = idx - g * grp_sz;
+    int h, j;
+    if (mid) {
+        const int h0 = 2 * g;
+        const int heads = min(2, BH - h0);             // the last group may hold one head
+        if (r == heads * per) {                        // the middle blocks of the group's heads
+            bh0 = h0;
+            qb0 = bh1 = qb1 = 0;
+            qb0 = (nqb - 2) / 2;
+            bh1 = h0 + 1;
+            qb1 = qb0;
+            nitems = heads;
+            return;
+        }
+        h = h0 + r / per;
+        j = r % per;
+    } else {
+        h = g;
+        j = r;
+    }
+    bh0 = bh1 = h;
+    if (j == 0) {
+        qb0 = qb1 = nqb - 1;
+        nitems = 1;
+    } else {
+        qb0 = nqb - 1 - j;  // nqb - 2 - p with p = j - 1
+        qb1 = j - 1;
+        nitems = 2;
+    }
+}
+
+template <int D, bool CAUSAL, bool PAIRED, int KS, bool BAL>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                         const __bf16* __restrict__ v, __bf16* __restrict__ o,
                         float* __restrict__ lse, int BH, int N, int nqb, float scale_log2)
 {
     static_assert(KS == 1 || (KS == 2 && !PAIRED), "key split only for one block per workgroup");
+    static_assert(!BAL || PAIRED, "balanced groups are run by the paired kernel");
     constexpr int kRowsWG = kBrBf16 / KS;  // query rows per workgroup
     using TL = Tile<D, kPPWaves>;
     constexpr int L = TL::kLoadsPerWave;
@@ -121,18 +167,23 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     // Work items: one query block per workgroup, or (PAIRED, causal) the two
     // blocks nqb-1-p and p of a head one after the other, so that every
     // workgroup has the same number of key tiles.
-    int first, second, nitems, bh;
-    if constexpr (PAIRED) {
-        block_coords<CAUSAL>(blockIdx.x, BH, (nqb + 1) / 2, second, bh);
+    int first, second, nitems, bh0, bh1;
+    if constexpr (BAL) {
+        balanced_items(blockIdx.x, BH, nqb, bh0, first, bh1, second, nitems);
+    } else if constexpr (PAIRED) {
+        block_coords<CAUSAL>(blockIdx.x, BH, (nqb + 1) / 2, second, bh0);
         first = nqb - 1 - second;
         nitems = first == second ? 1 : 2;
+        bh1 = bh0;
     } else {
-        block_coords<CAUSAL>(blockIdx.x, BH, nqb, first, bh);
+        block_coords<CAUSAL>(blockIdx.x, BH, nqb, first, bh0);
         second = first;
         nitems = 1;
+        bh1 = bh0;
     }
     for (int item = 0; item < nitems; ++item) {
     const int qb = item == 0 ? first : second;
+    const int bh = item == 0 ? bh0 : bh1;
     if (item) __syncthreads();  // the previous block's LDS reads are done
     const size_t head_off = (size_t)bh * (size_t)N * D;
     const __bf16* qh = q + head_off;
@@ -671,14 +722,17 @@ hipError_t launch_one(const __bf16* q, const __bf16* k, const __bf16* v, __bf16*
     const FwdPlan pl = fwd_plan(BH, N, CAUSAL);
     const dim3 grid((unsigned)pl.grid);
     if (pl.key_split == 2)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, false, 2>), grid, dim3(kPPThreads), 0,
-                           stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, false, 2, false>), grid, dim3(kPPThreads),
+                           0, stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
+    else if (CAUSAL && pl.balanced)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, CAUSAL, 1, CAUSAL>), grid,
+                           dim3(kPPThreads), 0, stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
     else if (CAUSAL && pl.paired)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, CAUSAL, 1>), grid, dim3(kPPThreads), 0,
-                           stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, CAUSAL, 1, false>), grid, dim3(kPPThreads),
+                           0, stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
     else
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, false, 1>), grid, dim3(kPPThreads), 0,
-                           stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, false, 1, false>), grid, dim3(kPPThreads),
+                           0, stream, q, k, v, o, lse, BH, N, pl.nqb, scale_log2);
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, flo
 struct FwdPlan {
     int key_split;      // 1 or 2
     bool paired;
+    bool balanced;      // causal blocks grouped so that every workgroup has nqb units of work
     int rows;           // query rows per block
     int nqb;            // query blocks per head
     long long grid;     // workgroups

@@ -22,12 +22,25 @@ constexpr int kPairMaxN = 8192;
 // loop (measured on B8 H12 N1024 d64 causal: 768 key-split workgroups
 // 43.0 us, 384 unpaired blocks 41.6 us, 192 paired blocks 31.4 us).
 constexpr long long kCUs = 256;
+// Causal grids whose pairs leave CUs idle and which the key split would run
+// in more than one round group the query blocks so that every workgroup
+// has exactly the heaviest block's work: block q of a head costs q + 1 units
+// (4 key tiles each), and the workgroups are {nqb-1}, {nqb-2-p, p} and, when
+// nqb is even, the middle blocks (nqb-2)/2 of two heads. nqb units per
+// workgroup instead of the pairs' nqb + 1, and about half a workgroup more
+// per head (GPT-2 shape: 240 workgroups of 4 units against 192 of 5).
+long long balanced_grid(long long BH, int nqb)
+{
+    const long long per = 1 + (nqb - 1) / 2;
+    return BH * per + (nqb % 2 == 0 ? (BH + 1) / 2 : 0);
+}
 
 }  // namespace
 
 FwdPlan fwd_plan(long long BH, int N, bool causal)
 {
     FwdPlan pl;
+    pl.balanced = false;
     pl.key_split = 1;
     pl.rows = kBrBf16;
     pl.nqb = (N + kBrBf16 - 1) / kBrBf16;
@@ -41,6 +54,10 @@ FwdPlan fwd_plan(long long BH, int N, bool causal)
         pl.rows = kBrBf16 / 2;
         pl.nqb = nqb2;
         pl.grid = BH * nqb2;
+    } else if (causal && pl.nqb > 1 && pl.grid < kCUs && balanced_grid(BH, pl.nqb) <= kCUs) {
+        pl.paired = true;
+        pl.balanced = true;
+        pl.grid = balanced_grid(BH, pl.nqb);
     }
     return pl;
 }

@@ -46,7 +46,10 @@ def test_tile_shape():
 @pytest.mark.parametrize("B,H,N,causal,expect", [
     # (workgroups, rows per block, paired)
     (4, 12, 512, 0, (192, 128, False)),     # BERT shape: 96 blocks of 256 rows -> key split
-    (8, 12, 1024, 1, (192, 256, True)),     # GPT-2 shape: 768 key-split blocks would take 3 rounds
+    (8, 12, 1024, 1, (240, 256, True)),     # GPT-2 shape: balanced groups (key split: 768, 3 rounds)
+    (1, 40, 2000, 1, (180, 256, True)),     # balanced, nqb = 8: 40 x 4 + 20 middle pairs
+    (3, 9, 1300, 1, (95, 256, True)),       # balanced, 27 heads: one middle block alone
+    (1, 33, 2300, 1, (165, 256, True)),     # balanced, nqb = 9 odd: no middles
     (2, 32, 8192, 1, (1024, 256, True)),    # long document: paired
     (1, 32, 32768, 1, (4096, 256, False)),  # very long context: one block per workgroup
     (1, 2, 65, 1, (2, 256, False)),         # one block either way: 256 rows

@@ -71,6 +71,23 @@ def test_paired_query_blocks(B, H, N, d):
     check_rows(q, k, v, True, 1.0 / math.sqrt(d), rows, f"paired N={N} d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", [(1, 40, 2000), (3, 9, 1300), (1, 33, 2300)])
+def test_balanced_causal_groups(B, H, N, d):
+    # Small causal grids whose key-split grid would take several rounds run
+    # groups of query blocks with equal work: {nqb-1}, {nqb-2-p, p} and, for
+    # even nqb, the middle blocks of two heads (27 heads: one alone; nqb = 9:
+    # none). Every output against the oracle.
+    grid, rows_per_block, paired = _grid(B, H, N, True)
+    nqb = (N + 255) // 256
+    per = 1 + (nqb - 1) // 2
+    assert rows_per_block == 256 and paired
+    assert grid == B * H * per + ((B * H + 1) // 2 if nqb % 2 == 0 else 0)
+    say(f"balanced groups B={B} H={H} N={N} d={d} causal ({grid} workgroups)")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=N + d + H)
+    check_full(q, k, v, True, 1.0 / math.sqrt(d), f"balanced N={N} d={d}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [129, 200, 257, 333, 700, 1000, 2100])
