@@ -59,6 +59,12 @@
 //    The tiles below the workgroup's diagonal run as straight-line steps
 //    without those conditions, each phase one basic block whose crossing
 //    values are pinned on both sides of the barrier.
+//  * Grids that would leave CUs idle (fa_plan.cpp decides, fa_fwd_grid
+//    reports): either 128-row blocks whose key tiles the two wave groups
+//    split, with the two partial (max, sum, output) states merged at the end
+//    [Flash Attention Optimization (aicomputerinstitute.com), "The fix: tile
+//    the computation..."], or, for causal grids, query blocks grouped so that
+//    every workgroup carries the heaviest block's work.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
