@@ -168,6 +168,57 @@ def test_random_shapes(B, H, N, d, causal):
     check_full(q, k, v, causal, 1.0 / math.sqrt(d), f"random N={N} d={d}")
 
 
+# Shapes drawn from a seeded generator (B 1-4, H 1-40, N 1-3000, d 64/128,
+# causal 60%) and kept ten per launch mode of fa_fwd: one 256-row block per
+# workgroup, 128-row key-split blocks, paired causal blocks and balanced
+# causal groups.
+_MODE_SHAPES = [
+    (2, 29, 1826, 128, False, "one"), (3, 7, 2584, 64, False, "one"),
+    (3, 33, 515, 128, False, "one"), (1, 35, 1613, 128, False, "one"),
+    (4, 8, 2678, 128, False, "one"), (3, 38, 2090, 64, False, "one"),
+    (3, 32, 2806, 128, False, "one"), (3, 7, 1584, 64, False, "one"),
+    (4, 3, 46, 128, True, "one"), (3, 34, 116, 64, True, "one"),
+    (3, 35, 164, 128, False, "key_split"), (3, 8, 468, 128, False, "key_split"),
+    (1, 1, 2635, 128, True, "key_split"), (1, 25, 730, 128, False, "key_split"),
+    (3, 13, 388, 64, False, "key_split"), (1, 1, 1931, 128, True, "key_split"),
+    (3, 1, 691, 128, False, "key_split"), (1, 40, 219, 128, False, "key_split"),
+    (2, 9, 1330, 128, True, "key_split"), (2, 6, 1891, 64, False, "key_split"),
+    (1, 29, 1051, 128, True, "paired"), (4, 26, 1823, 128, True, "paired"),
+    (3, 20, 1747, 128, True, "paired"), (2, 11, 1754, 128, True, "paired"),
+    (3, 31, 1587, 64, True, "paired"), (2, 31, 1657, 64, True, "paired"),
+    (4, 31, 1436, 128, True, "paired"), (2, 36, 1691, 128, True, "paired"),
+    (3, 37, 1435, 64, True, "paired"), (4, 31, 2579, 64, True, "paired"),
+    (1, 23, 2498, 64, True, "balanced"), (3, 32, 387, 64, True, "balanced"),
+    (1, 18, 2003, 128, True, "balanced"), (2, 7, 2469, 128, True, "balanced"),
+    (4, 20, 788, 64, True, "balanced"), (3, 14, 1867, 128, True, "balanced"),
+    (4, 10, 942, 128, True, "balanced"), (2, 10, 2928, 64, True, "balanced"),
+    (1, 24, 2900, 128, True, "balanced"), (1, 23, 2404, 64, True, "balanced"),
+]
+
+
+def _launch_mode(B, H, N, causal):
+    grid, rows_per_block, paired = _grid(B, H, N, causal)
+    nqb = (N + 255) // 256
+    if rows_per_block == 128:
+        return "key_split"
+    if paired and grid != B * H * ((nqb + 1) // 2):
+        return "balanced"
+    return "paired" if paired else "one"
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,mode", _MODE_SHAPES)
+def test_random_launch_modes(B, H, N, d, causal, mode):
+    # The launch mode the shape is filed under is the one fa_fwd picks; then
+    # sampled rows of every head, every block and tile edge included, against
+    # the oracle.
+    assert _launch_mode(B, H, N, causal) == mode
+    say(f"launch mode {mode}: B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=7 * N + 11 * H + B + d + causal)
+    edge = torch.tensor(_boundary_rows(N), dtype=torch.int64)
+    rows = torch.cat([sample_rows(N, 8, seed=N + H, heads=B * H), edge.expand(B * H, -1)], 1)
+    check_rows(q, k, v, causal, 1.0 / math.sqrt(d), rows, f"{mode} N={N} d={d} causal={causal}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp32_storage_path(d):
     say(f"fp32 storage B=2 H=2 N=300 d={d}")
