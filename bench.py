@@ -159,17 +159,19 @@ def ingest_counters(fetch_csv, write_csv, copy_mib, command, pass_="fwd"):
     return 0
 
 
-def gemm_reference(torch, stream, achieved_tflops, n=8192, iters=10):
+def gemm_reference(torch, stream, achieved_tflops, n=8192, iters=20, warmup=30):
     """Same-box reference for the MFMA rate: torch's bf16 GEMM (hipBLASLt) at
     n^3, timed with HIP events on the bench stream after the timed region. The
     2.5 PFLOP/s datasheet peak assumes a 2.4 GHz engine clock that dense MFMA
     work does not hold on these boards; this number says what a vendor GEMM
-    reaches on the same GPU in the same run."""
+    reaches on the same GPU in the same run. The GEMM gets as many warm-up
+    calls as the kernel's default: the engine clock dips and recovers over
+    the first few tens of milliseconds of dense MFMA work after a pause."""
     g = torch.Generator(device="cuda").manual_seed(0)
     a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
     b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
     with torch.cuda.stream(stream):
-        for _ in range(3):
+        for _ in range(warmup):
             c = a @ b
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -184,6 +186,96 @@ def gemm_reference(torch, stream, achieved_tflops, n=8192, iters=10):
     return {"what": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), same GPU and run",
             "tflops": round(tflops, 1), "ms": round(ms, 4),
             "kernel_over_reference": round(achieved_tflops / tflops, 4)}
+
+
+def engine_clock_sample():
+    """(engine clock MHz, socket power W) as rocm-smi reports them now, or
+    None for what it does not report. A read-only query."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "-g", "-P"], capture_output=True, text=True,
+                             timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None, None
+    m = re.search(r"sclk clock level:[^(]*\((\d+)\s*Mhz\)", out, re.I)
+    p = re.search(r"Power \(W\):\s*([\d.]+)", out)
+    return (int(m.group(1)) if m else None), (float(p.group(1)) if p else None)
+
+
+def sustained_run(torch, stream, call, seconds, ms_hint):
+    """Run `call` back to back on `stream` for about `seconds`, keeping the
+    queue full, while a thread samples the engine clock every ~0.5 s. Returns
+    the mean ms per call over the second half of the run (HIP events) and the
+    median clock and power of the samples taken in that half."""
+    import statistics
+    import threading
+    chunk = max(1, int(0.1 / max(ms_hint * 1e-3, 1e-6)))  # ~0.1 s of work per chunk
+    nchunks = max(6, int(seconds / 0.1))
+    samples, stop = [], threading.Event()
+    half = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            clk, pw = engine_clock_sample()
+            if half.is_set():
+                samples.append((clk, pw))
+            stop.wait(0.5)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    evs = []
+    with torch.cuda.stream(stream):
+        for c in range(nchunks):
+            for _ in range(chunk):
+                call()
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            evs.append(ev)
+            if c >= 3:
+                evs[c - 3].synchronize()  # at most ~0.3 s of work queued ahead
+            if c == nchunks // 2:
+                half.set()
+    evs[-1].synchronize()
+    stop.set()
+    th.join()
+    mid = nchunks // 2
+    ms = evs[mid].elapsed_time(evs[-1]) / ((nchunks - 1 - mid) * chunk)
+    clks = [c for c, _ in samples if c is not None]
+    pws = [p for _, p in samples if p is not None]
+    return {"seconds": round(seconds, 1), "calls_timed": (nchunks - 1 - mid) * chunk,
+            "ms_per_call": round(ms, 5),
+            "sclk_mhz": statistics.median(clks) if clks else None,
+            "power_w": statistics.median(pws) if pws else None, "clock_samples": len(clks)}
+
+
+def sustained_reference(torch, stream, step, seconds, ms_hint, flops, peak, gemm):
+    """--sustained: the pass's step back to back for `seconds` (timed over the
+    second half, engine clock sampled), then torch's 8192^3 bf16 GEMM the same
+    way when `gemm`. The datasheet peaks assume 2.4 GHz; `peak_at_clock`
+    scales the peak to the clock the step actually ran at."""
+    log(f"sustained run: {seconds:.1f} s of back-to-back calls, engine clock sampled ...")
+    r = sustained_run(torch, stream, step, seconds, ms_hint)
+    r["tflops"] = round(flops / (r["ms_per_call"] * 1e-3) / 1e12, 1)
+    if r["sclk_mhz"]:
+        r["peak_at_clock"] = round(peak * r["sclk_mhz"] / 2400.0, 1)
+        r["frac_at_clock"] = round(r["tflops"] / r["peak_at_clock"], 4)
+    log(f"sustained: {r['ms_per_call']:.4f} ms per call, {r['tflops']} TFLOP/s, "
+        f"engine clock {r['sclk_mhz']} MHz, power {r['power_w']} W")
+    if gemm:
+        n = 8192
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        out = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+        rg = sustained_run(torch, stream, lambda: torch.matmul(a, b, out=out), seconds, 1.0)
+        rg["tflops"] = round(2.0 * n ** 3 / (rg["ms_per_call"] * 1e-3) / 1e12, 1)
+        rg["what"] = f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)"
+        log(f"sustained GEMM: {rg['tflops']} TFLOP/s, engine clock {rg['sclk_mhz']} MHz, "
+            f"power {rg['power_w']} W")
+        r["gemm"] = rg
+        del a, b, out
+    return r
 
 
 def hbm_reference(torch, stream, achieved_gbs, mib=1024, iters=10):
@@ -541,6 +633,10 @@ def main(argv=None):
                          "stream: torch's bf16 GEMM (8192^3, hipBLASLt) for the bf16 fwd/bwd "
                          "passes (MFMA rate the chip sustains), torch's 1 GiB device copy for "
                          "the std and decode passes (HBM rate); 0 = skip")
+    ap.add_argument("--sustained", type=float, default=0.0,
+                    help="after the timed region, run the step back to back for this many "
+                         "seconds with the engine clock sampled by rocm-smi (and, for the "
+                         "bf16 passes, torch's 8192^3 GEMM the same way); 0 = skip")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB 3 times "
                          "(reference kernel for HBM counter calibration)")
@@ -772,6 +868,10 @@ def main(argv=None):
         result["mfma_reference"] = gemm_reference(torch, stream, achieved)
     if args.gemm_ref and stdp:
         result["hbm_reference"] = hbm_reference(torch, stream, sm_gbs)
+    if args.sustained > 0:
+        result["sustained"] = sustained_reference(
+            torch, stream, step, args.sustained, ms_per_step, flops,
+            PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS, not (fp8 or stdp))
     if args.cpu_budget > 0:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do_cpu, args.cpu_budget) if bwd
