@@ -59,7 +59,7 @@ PASS_SOURCES = {"fwd": ("fa_common.h", "fa_lds.h", "fa_fwd_bf16.hip"),
                 "decode": ("fa_common.h", "fa_decode.hip")}
 # Kernel names (substrings) rocprofv3 reports for each pass.
 PASS_KERNELS = {"fwd": ("fa_fwd_bf16_kernel",),
-                "bwd": ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"),
+                "bwd": ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_phased_kernel"),
                 "std": ("fa_std_softmax",),
                 "fp8": ("fa_fwd_fp8_kernel",),
                 "decode": ("fa_decode_split_kernel", "fa_decode_merge_kernel")}

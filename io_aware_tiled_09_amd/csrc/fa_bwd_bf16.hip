@@ -19,9 +19,14 @@
 //    dK^T += Q^T dS, whose A operands are transpose reads of the Q and dO
 //    tiles (ds_read_b64_tr_b16) -- the forward kernel's layout with the
 //    roles of queries and keys exchanged.
-//  * dq: one workgroup per 128 queries (4 waves x 32 rows), streaming K and
-//    V tiles like the forward kernel: S^T = K Q^T and dP^T = V dO^T, then
-//    dQ^T += K^T dS^T with K^T from transpose reads of the K tile.
+//  * dq: one workgroup per 128 queries (4 waves x 32 rows, two workgroups
+//    per CU), streaming K and V tiles like the forward kernel:
+//    S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T with K^T from
+//    transpose reads of the K tile. Grids of at least four rounds of
+//    workgroups run the phased form instead: 256 queries per workgroup in
+//    two phase-offset wave groups (the forward kernel's structure), one
+//    forming dS while the other runs the dQ and score MFMAs. Both forms
+//    accumulate in the same order, so their gradients are bitwise equal.
 //  * P is recomputed as exp2(s * scale*log2(e) - lse*log2(e)); masked and
 //    out-of-range entries are 0. dS is formed in fp32 and rounded to bf16 for
 //    its products; all products accumulate in fp32.
@@ -606,6 +611,358 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     if (qi < N) store_row<D>(dq + head_off + (size_t)qi * D, acc, scale, lh);
 }
 
+// ---------------------------------------------------------------- dq, phased
+// Grids of at least four rounds of workgroups (bwd_dq_phased): one workgroup
+// per 256 queries of a head, 8 wave64s of 32 query rows in two
+// phase-offset groups, as in the forward kernel (waves w and w + 4 share a
+// SIMD). Per key tile j (64 keys) a wave runs
+//   A(j): dS(j) = P(j) (dP(j) - D) from S(j) = Q K_j^T and dP(j) = dO V_j^T,
+//         P recomputed as exp2(S c - lse2), masked entries 0, dS rounded to
+//         bf16 (VALU and transcendental work only);
+//   B(j): dQ^T += K_j^T dS(j)^T (K_j^T by transpose reads), then S(j+1) and
+//         dP(j+1) (K and V fragments row-major): matrix work only.
+// Group 1 runs one phase behind group 0 and every phase ends with a
+// workgroup barrier, so on every SIMD one wave feeds the matrix core while
+// the other runs the VALU work. S^T and dP^T come out of the 32x32x16 MFMA
+// with one query per lane column, so dS is directly the B operand of the
+// dQ product. K and V tiles go straight into two rings of four LDS slots
+// (tile t in slot t % 4), loaded by the group in its VALU phase: in step j
+// group 0 loads V_{j+3} and group 1 loads K_{j+3} (K_t is read in B(t-1)
+// and B(t), up to global phase 2t + 2; V_t in B(t-1) only).
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = kDqWaves * 64;
+constexpr int kDqRows = kDqWaves * 32;  // queries per workgroup
+constexpr int kDqRing = 4;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_phased_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                             const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                             const float* __restrict__ lse, const float* __restrict__ delta,
+                             __bf16* __restrict__ dq, int BH, int N, int nqb,
+                             float scale_log2, float scale)
+{
+    using TL = Tile<D, kDqWaves>;
+    using TG = Tile<D, kDqWaves / 2>;
+    constexpr int L = TL::kLoadsPerWave;
+    constexpr int LG = TG::kLoadsPerWave;  // = 2L
+    __shared__ __attribute__((aligned(1024))) unsigned char kring[kDqRing][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vring[kDqRing][TL::kBytes];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int lane = tid & 63;
+    const int li = lane & 31;
+    const int lh = lane >> 5;
+
+    int qb, bh;
+    block_coords<CAUSAL>(blockIdx.x, BH, nqb, qb, bh);
+    const size_t head_off = (size_t)bh * (size_t)N * D;
+    const __bf16* kh = k + head_off;
+    const __bf16* vh = v + head_off;
+
+    const int q0 = qb * kDqRows;
+    const int qw0 = q0 + wave * 32;
+    const int qi = qw0 + li;
+
+
+    bf16x8 qf[D / 16], df[D / 16];  // this lane's Q and dO rows (B operands), set in the prologue
+    float lse2, dlt;                 // its lse * log2(e) and D
+    const int nkb_all = (N + kBc - 1) / kBc;
+    const int nkb = CAUSAL ? min(nkb_all, (q0 + kDqRows - 1) / kBc + 1) : nkb_all;
+
+    int ld_off[L], gl_off[LG];
+#pragma unroll
+    for (int it = 0; it < L; ++it) ld_off[it] = TL::load_offset(wave, it, lane);
+#pragma unroll
+    for (int it = 0; it < LG; ++it) gl_off[it] = TG::load_offset(wave & 3, it, lane);
+    // Buffer resource over tile t of `src`; a tile past the last one gets an
+    // empty range (nothing is read) so that the loads are still issued and
+    // the vmcnt arithmetic holds.
+    auto tile_rsrc = [&](const __bf16* src, int t) __attribute__((always_inline)) {
+        const int j0 = t * kBc;
+        const bool real = t < nkb;
+        const unsigned bytes = real ? (unsigned)min(kBc, N - j0) * TL::kRowBytes : 0u;
+        return buffer_rsrc(real ? src + (size_t)j0 * D : src, bytes);
+    };
+    auto issue = [&](const __bf16* src, int t, unsigned char* dst) __attribute__((always_inline)) {
+        const i32x4 rs = tile_rsrc(src, t);
+#pragma unroll
+        for (int it = 0; it < L; ++it)
+            lds_dma16(rs, ld_off[it], lds_addr(dst + (wave * L + it) * 1024));
+    };
+    auto issue_grp = [&](const __bf16* src, int t, unsigned char* dst) __attribute__((always_inline)) {
+        const i32x4 rs = tile_rsrc(src, t);
+        unsigned lb = lds_addr(dst + (wave & 3) * LG * 1024);
+        asm volatile("" : "+s"(lb));
+#pragma unroll
+        for (int it = 0; it < LG; ++it) lds_dma16(rs, gl_off[it], lb + it * 1024);
+    };
+    // Rows of a partial last tile past the sequence end are cleared once it
+    // has landed: their weights are 0, and 0 * NaN would leak.
+    auto clear_tail = [&](int t, unsigned char* dst) __attribute__((always_inline)) {
+        const int rows = N - t * kBc;
+        if (rows >= kBc) return;
+        for (int x = tid; x < (kBc - rows) * TL::kChunks; x += kDqThreads) {
+            const int row = rows + x / TL::kChunks;
+            *reinterpret_cast<bf16x8*>(dst + row * TL::kRowBytes + (x % TL::kChunks) * 16) = bf16x8{};
+        }
+    };
+
+    // Fragment offsets from three bases: chunk 2c + lh of a row sits at
+    // base ^ (c << 5) and the transpose reads of column block tt at
+    // base ^ (tt << 6) (the swizzle XORs chunk bits only and the ring bases
+    // are 1024-aligned); ring slot and sub-tile offsets are immediates.
+    unsigned kbase = lds_addr(kring[0]), vbase = lds_addr(vring[0]);
+    asm volatile("" : "+s"(kbase), "+s"(vbase));
+    unsigned k_row = kbase + TL::frag_offset(li, lh);
+    unsigned v_row = vbase + TL::frag_offset(li, lh);
+    unsigned k_tr[2] = {kbase + TL::tr_offset(0, 0, lane), kbase + TL::tr_offset(0, 1, lane)};
+
+    f32x16 acc[D / 32];  // dQ^T: rows d, column = query
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    f32x16 sc[kBc / 32], dp[kBc / 32];  // S^T and dP^T of the tile whose dS runs next
+    bf16x8 dsf[kBc / 32][2];             // dS of the current tile, from A(j) to B(j)
+
+    // S^T = K Q^T and dP^T = V dO^T of the tile in ring slot `slot`; the K
+    // and V fragments are read kDqReadAhead MFMAs ahead of their use.
+    constexpr int kSPMfmas = 2 * (kBc / 32) * (D / 16);
+    auto scores = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) {
+            sc[st] = f32x16{};
+            dp[st] = f32x16{};
+        }
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+            for (int st = 0; st < kBc / 32; ++st) {
+                const unsigned off = slot * TL::kBytes + st * 32 * TL::kRowBytes;
+                const bf16x8 ka = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                    (size_t)((k_row ^ ((unsigned)c << 5)) + off));
+                const bf16x8 va = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                    (size_t)((v_row ^ ((unsigned)c << 5)) + off));
+                sc[st] = mfma(ka, qf[c], sc[st]);
+                dp[st] = mfma(va, df[c], dp[st]);
+            }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDqReadAhead, 0);
+#pragma unroll
+        for (int i = 0; i < kSPMfmas - kDqReadAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kDqReadAhead, 0);
+    };
+    // dQ^T += K^T dS^T for the tile in ring slot `slot`: two transpose reads
+    // per MFMA, consecutive MFMAs on different accumulators.
+    constexpr int kDqMfmas = (D / 32) * (kBc / 16);
+    auto dq_update = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int tt = 0; tt < D / 32; ++tt) {
+                    const unsigned off = slot * TL::kBytes + (st * 32 + h2 * 16) * TL::kRowBytes;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(size_t)((k_tr[0] ^ ((unsigned)tt << 6)) + off));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(size_t)((k_tr[1] ^ ((unsigned)tt << 6)) + off));
+                    const s16x4 pair[2] = {lo, hi};
+                    bf16x8 ka;
+                    __builtin_memcpy(&ka, pair, sizeof(ka));
+                    acc[tt] = mfma(ka, dsf[st][h2], acc[tt]);
+                }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kDqReadAhead, 0);
+#pragma unroll
+        for (int i = 0; i < kDqMfmas - kDqReadAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kDqReadAhead, 0);
+    };
+
+    // ---- prologue: this lane's Q and dO rows (B operands) and statistics,
+    // then K_0..K_2 and V_0..V_2 in LDS, all landed before S(0) and dP(0)
+    {
+        const __bf16* qrow = q + head_off + (size_t)qi * D;
+        const __bf16* drow = dout + head_off + (size_t)qi * D;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            qf[c] = qi < N ? *reinterpret_cast<const bf16x8*>(qrow + c * 16 + lh * 8) : bf16x8{};
+            df[c] = qi < N ? *reinterpret_cast<const bf16x8*>(drow + c * 16 + lh * 8) : bf16x8{};
+        }
+    }
+    lse2 = qi < N ? lse[(size_t)bh * N + qi] * kLog2e : 0.f;
+    dlt = qi < N ? delta[(size_t)bh * N + qi] : 0.f;
+    // Retire the row loads here, visibly to the compiler's wait-count pass.
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    issue(kh, 0, kring[0]);
+    issue(vh, 0, vring[0]);
+    issue(kh, 1, kring[1]);
+    issue(vh, 1, vring[1]);
+    issue(kh, 2, kring[2]);
+    issue(vh, 2, vring[2]);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    if (nkb <= 3) {  // the partial tile, if any, is among these
+        clear_tail(nkb - 1, kring[nkb - 1]);
+        clear_tail(nkb - 1, vring[nkb - 1]);
+    }
+    __syncthreads();
+    scores(0);
+
+    // Phases. Global phase s: group 0 runs A(s/2) for even s and B(s/2) for
+    // odd s; group 1 runs one phase later. The group in its VALU phase loads
+    // one tile: V_{s/2+3} in even phases (group 0), K_{(s+5)/2} in odd ones
+    // (group 1), into the slot of the tile four back (V_{t-4} was last read in
+    // phase 2t - 8, K_{t-4} in phase 2t - 6). A tile t is first read in phase
+    // 2t - 1. Waits: at the end of its VALU phase a wave allows its loads of
+    // that phase and the one two before in flight (vmcnt(2 LG)); at the end
+    // of its MFMA phase only that step's (vmcnt(LG)). So group 1's K_t
+    // (issued in phase 2t - 5) has landed at the end of phase 2t - 2 and group
+    // 0's V_t (phase 2t - 6) at the end of phase 2t - 2 (its VALU phase end,
+    // three phases later), and that phase's barrier publishes both.
+    auto phase_loads = [&](int s) __attribute__((always_inline)) {
+        if ((s & 1) != grp) return;
+        if ((s & 1) == 0) {
+            const int t = s / 2 + 3;
+            issue_grp(vh, t, vring[t & 3]);
+        } else {
+            const int t = (s + 5) / 2;
+            issue_grp(kh, t, kring[t & 3]);
+        }
+    };
+    // The partial last tile (if any), issued in phases 2 nkb - 8 (V) and
+    // 2 nkb - 7 (K), is cleared at the end of phase 2 nkb - 4, after an extra
+    // barrier (only the loading groups' waits cover it), one phase before it
+    // is first read. Both groups reach that phase in the general steps.
+    const int tail_phase = (nkb > 3 && N % kBc != 0 && nkb == nkb_all) ? 2 * nkb - 4 : -1;
+    auto phase_end = [&](int s, auto mfma_phase) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(mfma_phase)::value) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LG));
+        else __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LG));
+        if (s == tail_phase) {
+            __syncthreads();
+            clear_tail(nkb - 1, kring[(nkb - 1) & 3]);
+            clear_tail(nkb - 1, vring[(nkb - 1) & 3]);
+        }
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto phase_end_plain = [&](auto mfma_phase) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(mfma_phase)::value) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LG));
+        else __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LG));
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // A(j): dS of tile j from sc and dp. In the general steps (the tiles on
+    // the causal diagonal and at the sequence end) every wave runs the masked
+    // form, also where all of a wave's keys are masked (its dS is then 0):
+    // the phase lasts as long as its slowest wave either way. Key
+    // score_key(st, r, lh) is visible iff its lane-independent part
+    // st*32 + (r/4)*8 + r%4 is at most one per-lane limit.
+    auto phase_a = [&](auto full, int kb) __attribute__((always_inline)) {
+        constexpr bool MASKED = !decltype(full)::value;
+        if (MASKED && kb >= nkb) return;
+        int lim = 0;
+        if constexpr (MASKED) {
+            lim = N - 1 - kb * kBc;
+            if constexpr (CAUSAL) lim = min(lim, qi - kb * kBc);
+            lim -= lh * 4;
+            asm volatile("" : "+v"(lim));
+        }
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][r], scale_log2, -lse2));
+                if constexpr (MASKED) {
+                    const int kc = st * 32 + (r >> 2) * 8 + (r & 3);
+                    p = kc <= lim ? p : 0.f;
+                }
+                dsf[st][r >> 3][r & 7] = (__bf16)(p * (dp[st][r] - dlt));
+            }
+    };
+    // B(j): dQ += K_j^T dS(j)^T, then S(j+1) and dP(j+1). The conditions are
+    // uniform over the workgroup.
+    auto phase_b = [&](auto full, int kb, int slot, int next_slot) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full)::value;
+        asm volatile("" : "+v"(k_row), "+v"(v_row), "+v"(k_tr[0]), "+v"(k_tr[1]));
+        if (FULL || kb < nkb) dq_update(slot);
+        if (FULL || kb + 1 < nkb) scores(next_slot);
+    };
+    // Values that cross a phase boundary pass through empty volatile asm on
+    // both sides of its barrier in the straight-line steps: A -> B dS, B -> A
+    // the next tile's S and dP and the accumulators.
+    auto pin_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) asm volatile("" : "+v"(dsf[st][0]), "+v"(dsf[st][1]));
+    };
+    auto pin_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < kBc / 32; ++st) asm volatile("" : "+v"(sc[st]), "+v"(dp[st]));
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) asm volatile("" : "+v"(acc[t]));
+    };
+    auto step = [&](auto ring, int kb) __attribute__((always_inline)) {
+        constexpr int R = decltype(ring)::value;
+        const int s = 2 * kb + grp;
+        phase_loads(s);
+        phase_a(std::false_type{}, kb);
+        phase_end(s, std::false_type{});
+        phase_b(std::false_type{}, kb, R, (R + 1) & 3);
+        phase_end(s + 1, std::true_type{});
+    };
+    // Steps that every wave runs whole: tile j below the workgroup's first
+    // query (causal) and inside N, tile j + 1 visible to every wave, and the
+    // partial tile's clear still ahead. Phase 2 kb + grp is this wave's
+    // loading phase: group 0 loads V_{kb+3}, group 1 K_{kb+3}.
+    auto step_full = [&](auto ring, int kb) __attribute__((always_inline)) {
+        constexpr int R = decltype(ring)::value;
+        if (grp == 0) issue_grp(vh, kb + 3, vring[(R + 3) & 3]);
+        else issue_grp(kh, kb + 3, kring[(R + 3) & 3]);
+        phase_a(std::true_type{}, kb);
+        pin_a();
+        phase_end_plain(std::false_type{});
+        pin_a();
+        phase_b(std::true_type{}, kb, R, (R + 1) & 3);
+        pin_b();
+        phase_end_plain(std::true_type{});
+        pin_b();
+    };
+
+    if (grp == 1) phase_end(0, std::false_type{});  // group 1's idle first phase
+    int kb = 0;
+    const int kb_full = min(CAUSAL ? q0 / kBc : nkb - 1, min(N / kBc, nkb - 3));
+    for (; kb + 4 <= kb_full; kb += 4) {
+        step_full(std::integral_constant<int, 0>{}, kb);
+        step_full(std::integral_constant<int, 1>{}, kb + 1);
+        step_full(std::integral_constant<int, 2>{}, kb + 2);
+        step_full(std::integral_constant<int, 3>{}, kb + 3);
+    }
+    // Four tiles per iteration; steps past the last tile only issue their
+    // (empty) loads and meet the barriers.
+    for (; kb < nkb; kb += 4) {
+        step(std::integral_constant<int, 0>{}, kb);
+        step(std::integral_constant<int, 1>{}, kb + 1);
+        step(std::integral_constant<int, 2>{}, kb + 2);
+        step(std::integral_constant<int, 3>{}, kb + 3);
+    }
+    // Group 0 stores its rows during group 1's last phase, then meets that
+    // phase's barrier; no load may still be landing when the workgroup ends.
+    if (grp == 0) {
+        if (qi < N) store_row<D>(dq + head_off + (size_t)qi * D, acc, scale, lh);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    if (grp == 1 && qi < N) store_row<D>(dq + head_off + (size_t)qi * D, acc, scale, lh);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_one(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
                           const float* lse, const __bf16* dout, __bf16* dq, __bf16* dk,
@@ -619,8 +976,15 @@ hipError_t launch_bwd_one(const __bf16* q, const __bf16* k, const __bf16* v, con
     const dim3 grid((unsigned)((long long)BH * nblk));
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(kDkdvThreads), 0, stream, q, k,
                        v, dout, lse, delta, dk, dv, BH, N, nblk, scale_log2, scale);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, q, k, v,
-                       dout, lse, delta, dq, BH, N, nblk, scale_log2, scale);
+    if (bwd_dq_phased(BH, N)) {
+        const int nqb = (N + kDqRows - 1) / kDqRows;
+        hipLaunchKernelGGL((fa_bwd_dq_phased_kernel<D, CAUSAL>),
+                           dim3((unsigned)((long long)BH * nqb)), dim3(kDqThreads), 0, stream, q,
+                           k, v, dout, lse, delta, dq, BH, N, nqb, scale_log2, scale);
+    } else {
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, q,
+                           k, v, dout, lse, delta, dq, BH, N, nblk, scale_log2, scale);
+    }
     return hipGetLastError();
 }
 

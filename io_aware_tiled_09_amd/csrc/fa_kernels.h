@@ -26,6 +26,9 @@ struct FwdPlan {
     long long grid;     // workgroups
 };
 FwdPlan fwd_plan(long long BH, int N, bool causal);
+// Whether the backward's dQ runs the phased 256-query kernel (else the
+// 128-query one).
+bool bwd_dq_phased(long long BH, int N);
 hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                       int BH, int N, int d, float scale_log2, bool causal, hipStream_t stream);
 // Backward pass (bf16 tensors, fp32 lse); delta: BH*N floats of workspace.

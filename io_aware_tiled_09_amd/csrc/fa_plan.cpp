@@ -1,5 +1,5 @@
-// Launch shape of the bf16 forward (host code: the kernel file launches by
-// it, the C ABI reports it).
+// Launch shapes of the bf16 forward (host code: the kernel file launches by
+// it, the C ABI reports it) and the choice of the backward's dQ kernel.
 #include "fa_kernels.h"
 
 namespace fa {
@@ -60,6 +60,21 @@ FwdPlan fwd_plan(long long BH, int N, bool causal)
         pl.grid = balanced_grid(BH, pl.nqb);
     }
     return pl;
+}
+
+// The phased dQ kernel (256 queries and one workgroup per CU, two
+// phase-offset wave groups) runs grids of at least four rounds of
+// workgroups; smaller grids run the 128-query kernel with two workgroups per
+// CU, whose workgroups overlap one another's prologue and epilogue. Measured
+// (whole backward call, gradients bitwise equal; 128-query -> phased):
+// B2 H32 N8192 d128 causal (2048 workgroups of 256 queries) 3421 -> 3345-3353
+// us, B1 H32 N16384 causal (2048) 6399 -> 6231 us, B2 H32 N4096 non-causal
+// (1024) 1676 -> 1634 us; B4 H16 N2048 d128 causal (512) 297.2 -> 303.3 us,
+// B8 H16 N1024 d64 causal (512) 139.2 -> 140.2 us, B8 H12 N1024 d64 causal
+// (384) 111.4 -> 116.9 us, B4 H12 N512 d64 (96) 28.4 -> 32.4 us.
+bool bwd_dq_phased(long long BH, int N)
+{
+    return BH * ((N + 255) / 256) >= 4 * kCUs;
 }
 
 }  // namespace fa

@@ -38,6 +38,23 @@ def test_bwd_ragged_multi_block(d, causal):
     check_bwd_full(q, k, v, do, causal, 1.0 / math.sqrt(d), "N=333")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", [(2, 64, 2100), (16, 64, 200), (16, 64, 100)])
+def test_bwd_phased_dq(B, H, N, d, causal):
+    # Grids of at least 1024 query blocks of 256 rows run dQ in the phased
+    # kernel: N = 2100 ends in a 52-row query block and a 52-key tile, cleared
+    # in the phase loop; N = 200 has four key tiles, the partial one cleared at
+    # the first phase that may; N = 100 has two, cleared in the prologue.
+    # Every row of three heads against the oracle.
+    heads = [0, (B * H) // 2 + 1, B * H - 1]
+    say(f"bwd phased dQ B={B} H={H} N={N} d={d} causal={causal}, heads {heads}")
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=N + d + causal)
+    do = make_dout(B=B, H=H, N=N, d=d, seed=N + d + causal)
+    check_bwd_full(q, k, v, do, causal, 1.0 / math.sqrt(d), f"phased N={N} d={d} causal={causal}",
+                   heads=heads)
+
+
 @pytest.mark.parametrize("scale", [0.05, 0.3])
 def test_bwd_explicit_scale(scale):
     say(f"bwd scale={scale} B=1 H=3 N=300 d=64 causal")
