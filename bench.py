@@ -194,19 +194,25 @@ def gemm_reference(torch, stream, n=8192, iters=20, warmup=30):
             "tflops": round(tflops, 1), "ms": round(ms, 4)}
 
 
+def parse_engine_clock(text):
+    """(engine clock MHz, socket power W) from the text of `rocm-smi -g -P`,
+    None for what the text does not hold."""
+    import re
+    m = re.search(r"sclk clock level:[^(]*\((\d+)\s*Mhz\)", text, re.I)
+    p = re.search(r"Power \(W\):\s*([\d.]+)", text)
+    return (int(m.group(1)) if m else None), (float(p.group(1)) if p else None)
+
+
 def engine_clock_sample():
     """(engine clock MHz, socket power W) as rocm-smi reports them now, or
     None for what it does not report. A read-only query."""
-    import re
     import subprocess
     try:
         out = subprocess.run(["rocm-smi", "-g", "-P"], capture_output=True, text=True,
                              timeout=30).stdout
     except (OSError, subprocess.SubprocessError):
         return None, None
-    m = re.search(r"sclk clock level:[^(]*\((\d+)\s*Mhz\)", out, re.I)
-    p = re.search(r"Power \(W\):\s*([\d.]+)", out)
-    return (int(m.group(1)) if m else None), (float(p.group(1)) if p else None)
+    return parse_engine_clock(out)
 
 
 def sustained_run(torch, stream, call, seconds, ms_hint):

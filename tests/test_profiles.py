@@ -75,3 +75,15 @@ def test_traffic_is_reported_only_for_its_workload(bench, pass_):
 def test_bench_refuses_more_than_one_gpu(bench, capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_engine_clock_parser(bench):
+    # `bench.py --sustained` reads the engine clock from rocm-smi's text; the
+    # lines below are the two forms seen on the boxes (clock only, and with a
+    # power line).
+    text = ("============================ ROCm System Management Interface "
+            "============================\nGPU[0]\t\t: sclk clock level: 1 (1633Mhz)\n")
+    assert bench.parse_engine_clock(text) == (1633, None)
+    text2 = (text + "GPU[0]\t\t: Current Socket Graphics Package Power (W): 1012.5\n")
+    assert bench.parse_engine_clock(text2) == (1633, 1012.5)
+    assert bench.parse_engine_clock("WARNING: AMD GPU device(s) is/are in a low-power state") == (None, None)
