@@ -646,10 +646,11 @@ def main(argv=None):
                          "(MFMA rate the chip sustains; it also takes the board through the "
                          "clock dip after idle), torch's 1 GiB device copy after the timed "
                          "region of the std and decode passes (HBM rate); 0 = skip")
-    ap.add_argument("--sustained", type=float, default=0.0,
+    ap.add_argument("--sustained", type=float, default=3.0,
                     help="after the timed region, run the step back to back for this many "
                          "seconds with the engine clock sampled by rocm-smi (and, for the "
-                         "bf16 passes, torch's 8192^3 GEMM the same way); 0 = skip")
+                         "bf16 passes, torch's 8192^3 GEMM the same way): the rate and the "
+                         "clock under sustained load, beside the K timed calls; 0 = skip")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB 3 times "
                          "(reference kernel for HBM counter calibration)")
