@@ -821,9 +821,10 @@ void fa_bwd_dq_phased_kernel(const __bf16* __restrict__ q, const __bf16* __restr
     // 2t - 1. Waits: at the end of its VALU phase a wave allows its loads of
     // that phase and the one two before in flight (vmcnt(2 LG)); at the end
     // of its MFMA phase only that step's (vmcnt(LG)). So group 1's K_t
-    // (issued in phase 2t - 5) has landed at the end of phase 2t - 2 and group
-    // 0's V_t (phase 2t - 6) at the end of phase 2t - 2 (its VALU phase end,
-    // three phases later), and that phase's barrier publishes both.
+    // (issued in phase 2t - 5) has landed at the end of phase 2t - 2, its
+    // MFMA phase end, and group 0's V_t (issued in phase 2t - 6) at the end
+    // of the same phase, its VALU phase end, and that phase's barrier
+    // publishes both.
     auto phase_loads = [&](int s) __attribute__((always_inline)) {
         if ((s & 1) != grp) return;
         if ((s & 1) == 0) {
@@ -918,9 +919,11 @@ void fa_bwd_dq_phased_kernel(const __bf16* __restrict__ q, const __bf16* __restr
         phase_end(s + 1, std::true_type{});
     };
     // Steps that every wave runs whole: tile j below the workgroup's first
-    // query (causal) and inside N, tile j + 1 visible to every wave, and the
-    // partial tile's clear still ahead. Phase 2 kb + grp is this wave's
-    // loading phase: group 0 loads V_{kb+3}, group 1 K_{kb+3}.
+    // query (causal) and inside N, so A(j) needs no mask; tile j + 1 below
+    // nkb - 2, so every wave forms its scores in B(j) (the next step masks
+    // them if it must) and the partial tile's clear is still ahead. Phase
+    // 2 kb + grp is this wave's loading phase: group 0 loads V_{kb+3},
+    // group 1 K_{kb+3}.
     auto step_full = [&](auto ring, int kb) __attribute__((always_inline)) {
         constexpr int R = decltype(ring)::value;
         if (grp == 0) issue_grp(vh, kb + 3, vring[(R + 3) & 3]);
