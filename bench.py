@@ -195,41 +195,65 @@ def gemm_reference(torch, stream, n=8192, iters=20, warmup=30):
 
 
 def parse_engine_clock(text):
-    """(engine clock MHz, socket power W) from the text of `rocm-smi -g -P`,
-    None for what the text does not hold."""
+    """Engine clock in MHz from the text of a `pp_dpm_sclk` file (one line
+    per clock level, the current one marked with '*'), or None."""
     import re
-    m = re.search(r"sclk clock level:[^(]*\((\d+)\s*Mhz\)", text, re.I)
-    p = re.search(r"Power \(W\):\s*([\d.]+)", text)
-    return (int(m.group(1)) if m else None), (float(p.group(1)) if p else None)
+    for line in text.splitlines():
+        if "*" in line:
+            m = re.search(r"(\d+)\s*Mhz", line, re.I)
+            if m:
+                return int(m.group(1))
+    return None
 
 
-def engine_clock_sample():
-    """(engine clock MHz, socket power W) as rocm-smi reports them now, or
-    None for what it does not report. A read-only query."""
-    import subprocess
+def engine_clock_path(torch):
+    """sysfs file that lists the engine clock levels of the GPU that torch
+    calls cuda:0 (the kernel driver's pp_dpm_sclk under its PCI address), or
+    the only such file when the address is not there, else None."""
+    import glob
+    import os
     try:
-        out = subprocess.run(["rocm-smi", "-g", "-P"], capture_output=True, text=True,
-                             timeout=30).stdout
-    except (OSError, subprocess.SubprocessError):
+        pr = torch.cuda.get_device_properties(0)
+        addr = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        path = f"/sys/bus/pci/devices/{addr}/pp_dpm_sclk"
+        if os.path.exists(path):
+            return path
+    except (AttributeError, RuntimeError):
+        pass
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return paths[0] if len(paths) == 1 else None
+
+
+def engine_clock_sample(path):
+    """(engine clock MHz, None) read from `path`: a plain file read, with no
+    subprocess, so nothing is started from this process, which has
+    initialised the GPU. (None, None) where it cannot be read."""
+    if path is None:
         return None, None
-    return parse_engine_clock(out)
+    try:
+        with open(path) as f:
+            return parse_engine_clock(f.read()), None
+    except OSError:
+        return None, None
 
 
 def sustained_run(torch, stream, call, seconds, ms_hint):
     """Run `call` back to back on `stream` for about `seconds`, keeping the
     queue full, while a thread samples the engine clock every ~0.5 s. Returns
     the mean ms per call over the second half of the run (HIP events) and the
-    median clock and power of the samples taken in that half."""
+    median clock of the samples taken in that half (power: not sampled from
+    sysfs, kept as None)."""
     import statistics
     import threading
     chunk = max(1, int(0.1 / max(ms_hint * 1e-3, 1e-6)))  # ~0.1 s of work per chunk
     nchunks = max(6, int(seconds / 0.1))
     samples, stop = [], threading.Event()
     half = threading.Event()
+    path = engine_clock_path(torch)
 
     def sampler():
         while not stop.is_set():
-            clk, pw = engine_clock_sample()
+            clk, pw = engine_clock_sample(path)
             if half.is_set():
                 samples.append((clk, pw))
             stop.wait(0.5)
@@ -648,7 +672,7 @@ def main(argv=None):
                          "region of the std and decode passes (HBM rate); 0 = skip")
     ap.add_argument("--sustained", type=float, default=3.0,
                     help="after the timed region, run the step back to back for this many "
-                         "seconds with the engine clock sampled by rocm-smi (and, for the "
+                         "seconds with the engine clock sampled from sysfs (and, for the "
                          "bf16 passes, torch's 8192^3 GEMM the same way): the rate and the "
                          "clock under sustained load, beside the K timed calls; 0 = skip")
     ap.add_argument("--copy-kernel-mib", type=int, default=0,

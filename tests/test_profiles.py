@@ -78,12 +78,10 @@ def test_bench_refuses_more_than_one_gpu(bench, capsys):
 
 
 def test_engine_clock_parser(bench):
-    # `bench.py --sustained` reads the engine clock from rocm-smi's text; the
-    # lines below are the two forms seen on the boxes (clock only, and with a
-    # power line).
-    text = ("============================ ROCm System Management Interface "
-            "============================\nGPU[0]\t\t: sclk clock level: 1 (1633Mhz)\n")
-    assert bench.parse_engine_clock(text) == (1633, None)
-    text2 = (text + "GPU[0]\t\t: Current Socket Graphics Package Power (W): 1012.5\n")
-    assert bench.parse_engine_clock(text2) == (1633, 1012.5)
-    assert bench.parse_engine_clock("WARNING: AMD GPU device(s) is/are in a low-power state") == (None, None)
+    # `bench.py --sustained` reads the engine clock from the kernel driver's
+    # pp_dpm_sclk file: one line per clock level, '*' on the current one.
+    assert bench.parse_engine_clock("0: 500Mhz\n1: 1633Mhz *\n2: 2400Mhz\n") == 1633
+    assert bench.parse_engine_clock("S: 130Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 130
+    assert bench.parse_engine_clock("0: 500Mhz\n1: 2400Mhz\n") is None
+    assert bench.engine_clock_sample(None) == (None, None)
+    assert bench.engine_clock_sample("/nonexistent/pp_dpm_sclk") == (None, None)
