@@ -206,54 +206,81 @@ def parse_engine_clock(text):
     return None
 
 
-def engine_clock_path(torch):
-    """sysfs file that lists the engine clock levels of the GPU that torch
-    calls cuda:0 (the kernel driver's pp_dpm_sclk under its PCI address), or
-    the only such file when the address is not there, else None."""
+def gpu_sysfs_dir(torch):
+    """sysfs directory of the GPU that torch calls cuda:0 (its PCI device
+    directory, which holds the kernel driver's pp_dpm_sclk and hwmon files),
+    or the only DRM card's device directory when the address is not there,
+    else None."""
     import glob
     import os
     try:
         pr = torch.cuda.get_device_properties(0)
         addr = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
-        path = f"/sys/bus/pci/devices/{addr}/pp_dpm_sclk"
-        if os.path.exists(path):
+        path = f"/sys/bus/pci/devices/{addr}"
+        if os.path.exists(os.path.join(path, "pp_dpm_sclk")):
             return path
     except (AttributeError, RuntimeError):
         pass
     paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
-    return paths[0] if len(paths) == 1 else None
+    return os.path.dirname(paths[0]) if len(paths) == 1 else None
 
 
-def engine_clock_sample(path):
-    """(engine clock MHz, None) read from `path`: a plain file read, with no
-    subprocess, so nothing is started from this process, which has
-    initialised the GPU. (None, None) where it cannot be read."""
-    if path is None:
+def _read_microwatts(dev_dir, name):
+    """A hwmon power file of the device in W (the files hold microwatts), or
+    None."""
+    import glob
+    if dev_dir is None:
+        return None
+    for path in sorted(glob.glob(f"{dev_dir}/hwmon/hwmon*/{name}")):
+        try:
+            with open(path) as f:
+                return int(f.read().strip()) / 1e6
+        except (OSError, ValueError):
+            continue
+    return None
+
+
+def engine_clock_sample(dev_dir):
+    """(engine clock MHz, board power W) of the GPU under `dev_dir`, read from
+    the kernel driver's sysfs files (pp_dpm_sclk; hwmon power1_average, else
+    power1_input): plain file reads, with no subprocess, so nothing is
+    started from this process, which has initialised the GPU. None for what
+    cannot be read."""
+    if dev_dir is None:
         return None, None
     try:
-        with open(path) as f:
-            return parse_engine_clock(f.read()), None
+        with open(f"{dev_dir}/pp_dpm_sclk") as f:
+            mhz = parse_engine_clock(f.read())
     except OSError:
-        return None, None
+        mhz = None
+    watts = _read_microwatts(dev_dir, "power1_average")
+    if watts is None:
+        watts = _read_microwatts(dev_dir, "power1_input")
+    return mhz, watts
+
+
+def power_cap_watts(dev_dir):
+    """The board's power cap in W (hwmon power1_cap), or None."""
+    return _read_microwatts(dev_dir, "power1_cap")
 
 
 def sustained_run(torch, stream, call, seconds, ms_hint):
     """Run `call` back to back on `stream` for about `seconds`, keeping the
     queue full, while a thread samples the engine clock every ~0.5 s. Returns
     the mean ms per call over the second half of the run (HIP events) and the
-    median clock of the samples taken in that half (power: not sampled from
-    sysfs, kept as None)."""
+    median clock and board power of the samples taken in that half, with the
+    board's power cap."""
     import statistics
     import threading
     chunk = max(1, int(0.1 / max(ms_hint * 1e-3, 1e-6)))  # ~0.1 s of work per chunk
     nchunks = max(6, int(seconds / 0.1))
     samples, stop = [], threading.Event()
     half = threading.Event()
-    path = engine_clock_path(torch)
+    dev_dir = gpu_sysfs_dir(torch)
 
     def sampler():
         while not stop.is_set():
-            clk, pw = engine_clock_sample(path)
+            clk, pw = engine_clock_sample(dev_dir)
             if half.is_set():
                 samples.append((clk, pw))
             stop.wait(0.5)
@@ -282,7 +309,8 @@ def sustained_run(torch, stream, call, seconds, ms_hint):
     return {"seconds": round(seconds, 1), "calls_timed": (nchunks - 1 - mid) * chunk,
             "ms_per_call": round(ms, 5),
             "sclk_mhz": statistics.median(clks) if clks else None,
-            "power_w": statistics.median(pws) if pws else None, "clock_samples": len(clks)}
+            "power_w": statistics.median(pws) if pws else None,
+            "power_cap_w": power_cap_watts(dev_dir), "clock_samples": len(clks)}
 
 
 def sustained_reference(torch, stream, step, seconds, ms_hint, flops, peak, gemm):

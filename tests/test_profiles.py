@@ -84,4 +84,18 @@ def test_engine_clock_parser(bench):
     assert bench.parse_engine_clock("S: 130Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 130
     assert bench.parse_engine_clock("0: 500Mhz\n1: 2400Mhz\n") is None
     assert bench.engine_clock_sample(None) == (None, None)
-    assert bench.engine_clock_sample("/nonexistent/pp_dpm_sclk") == (None, None)
+    assert bench.engine_clock_sample("/nonexistent") == (None, None)
+
+
+def test_engine_clock_sample_reads_sysfs_layout(bench, tmp_path):
+    # the driver's layout: pp_dpm_sclk in the device directory, power in
+    # microwatts under hwmon/hwmonN
+    (tmp_path / "pp_dpm_sclk").write_text("S: 1708Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    hw = tmp_path / "hwmon" / "hwmon3"
+    hw.mkdir(parents=True)
+    (hw / "power1_input").write_text("1012500000\n")
+    (hw / "power1_cap").write_text("1400000000\n")
+    assert bench.engine_clock_sample(str(tmp_path)) == (1708, 1012.5)
+    assert bench.power_cap_watts(str(tmp_path)) == 1400.0
+    (hw / "power1_average").write_text("998000000\n")
+    assert bench.engine_clock_sample(str(tmp_path)) == (1708, 998.0)
