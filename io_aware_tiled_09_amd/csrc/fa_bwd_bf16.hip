@@ -11,12 +11,13 @@
 //
 // gfx950 mapping (this file's own design): three kernels, no atomics.
 //  * delta: D_i = sum_t dO_it O_it per row into a workspace (HBM-bound).
-//  * dkdv: one workgroup per 128 keys of a head (4 waves x 32 keys); the
-//    wave keeps its K and V rows as MFMA B operands in VGPRs and streams
-//    64-query tiles of Q and dO through LDS. S = Q K^T and dP = dO V^T come
-//    out of v_mfma_f32_32x32x16_bf16 with one key per lane column, so P and
-//    dS (bf16) are directly the B operands of dV^T += dO^T P and
-//    dK^T += Q^T dS, whose A operands are transpose reads of the Q and dO
+//  * dkdv: one workgroup per 128 keys of a head, 8 waves: 4 key groups of
+//    32, each served by a pair of waves (one keeps the group's K rows, the
+//    other its V rows, as MFMA B operands in VGPRs); 64-query tiles of Q and
+//    dO stream through LDS. S = Q K^T and dP = dO V^T come out of
+//    v_mfma_f32_32x32x16_bf16 with one key per lane column, so P and dS
+//    (bf16) are directly the B operands of dV^T += dO^T P and
+//    dK^T += Q^T dS, whose A operands are transpose reads of the dO and Q
 //    tiles (ds_read_b64_tr_b16) -- the forward kernel's layout with the
 //    roles of queries and keys exchanged.
 //  * dq: one workgroup per 128 queries (4 waves x 32 rows, two workgroups
@@ -131,8 +132,9 @@ __device__ inline void clear_tile_tail(int t, int N, unsigned char* dst, int tid
 // The pair is software-pipelined by one tile and each step has two phases:
 // in phase 1 the P-wave runs dV(t) and S(t+1) on the matrix core while the
 // dS-wave forms dS(t); in phase 2 the dS-wave runs dK(t) and dP(t+1) while the
-// P-wave forms P(t+1). On every SIMD one wave of the pair feeds the matrix
-// core while the other works on the VALU, and the barrier between the phases
+// P-wave forms P(t+1). On every SIMD (a P-wave and the dS-wave of another
+// group) one wave feeds the matrix core while the other works on the VALU,
+// and the barrier between the phases
 // also orders the reads of P(t) before the writes of P(t+1), so P needs one
 // LDS buffer. Q and dO tiles use three (t, t+1 in use, t+2 loading).
 constexpr int kDkdvWaves = 8;
