@@ -55,6 +55,40 @@ def test_bwd_phased_dq(B, H, N, d, causal):
                    heads=heads)
 
 
+def _bwd_random_shapes(seed=20261203):
+    # Eight small shapes (B, H 1-3, N 1-2000), then four whose grids of
+    # 256-row query blocks reach four rounds of the CUs, so that dQ runs in
+    # the phased kernel (B = 4, H 24-40, N from the smallest such length to
+    # 700 past it, at most 3000).
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(8):
+        out.append((rng.randint(1, 3), rng.randint(1, 3), rng.randint(1, 2000),
+                    rng.choice([64, 128]), rng.choice([False, True])))
+    for _ in range(4):
+        B, H = 4, rng.randint(24, 40)
+        nqb = -(-1024 // (B * H))
+        N = rng.randint((nqb - 1) * 256 + 1, min(nqb * 256 + 700, 3000))
+        N = max(N, (nqb - 1) * 256 + 1)
+        out.append((B, H, N, rng.choice([64, 128]), rng.choice([False, True])))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", _bwd_random_shapes())
+def test_bwd_random_shapes(B, H, N, d, causal):
+    # Seeded shapes with ragged last query blocks and key tiles; every row of
+    # the first and last head against the oracle.
+    phased = B * H * -(-N // 256) >= 1024
+    heads = [0, B * H - 1] if B * H > 1 else [0]
+    say(f"bwd random B={B} H={H} N={N} d={d} causal={causal} "
+        f"({'phased' if phased else '128-query'} dQ), heads {heads}")
+    seed = B * 1000 + H * 100 + N + d
+    q, k, v = make_qkv(B=B, H=H, N=N, d=d, seed=seed)
+    do = make_dout(B=B, H=H, N=N, d=d, seed=seed)
+    check_bwd_full(q, k, v, do, causal, 1.0 / math.sqrt(d), f"random N={N} d={d}", heads=heads)
+
+
 @pytest.mark.parametrize("scale", [0.05, 0.3])
 def test_bwd_explicit_scale(scale):
     say(f"bwd scale={scale} B=1 H=3 N=300 d=64 causal")
