@@ -177,3 +177,12 @@ def check_bwd_sampled(q, k, v, dout, causal, scale, heads, qrows, krows, label="
         gh = g.reshape(B * H, N, d)[hs]
         out.append(torch.gather(gh, 1, rows.unsqueeze(-1).expand(-1, -1, d)).numpy())
     return assert_grads_close(out, ref, label, **bounds)
+
+
+def fp8_random_shapes(n=8, seed=808):
+    """Seeded (B, H, N, causal) shapes of the FP8 random-shape parity test
+    (d = 128), shared with the CPU derivation of the FP8 bound."""
+    import random
+    rng = random.Random(seed)
+    return [(rng.randint(1, 3), rng.randint(1, 4), rng.randint(1, 3000), rng.choice([False, True]))
+            for _ in range(n)]

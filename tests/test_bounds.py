@@ -25,7 +25,7 @@ from io_aware_tiled_09_amd.inputs import WORKLOADS, make_dout, make_qkv, make_qk
 
 import _emulate as E
 from _parity import (GRAD_LONG_MAX_REL, GRAD_MAX_REL, GRAD_MEAN_REL, GRAD_SPIKY_MAX_REL,
-                     GRAD_SPIKY_MEAN_REL, O_MAX_ABS, grad_errors)
+                     GRAD_SPIKY_MEAN_REL, O_MAX_ABS, fp8_random_shapes, grad_errors)
 
 
 def _head(x, bh):
@@ -155,6 +155,8 @@ def _fp8_cases():
         yield make_qkv_fp8(name, B=2, H=4, d=128), True, 128 ** -0.5
     codes, sc = make_qkv_fp8(B=1, H=3, N=300, d=128, seed=77)
     yield (codes, (sc[0] * 3.0, sc[1] * 0.5, sc[2] * 2.0)), True, 0.3
+    for B, H, N, causal in fp8_random_shapes():
+        yield make_qkv_fp8(B=B, H=H, N=N, d=128, seed=B * 1000 + H * 100 + N), causal, 128 ** -0.5
 
 
 def test_fp8_bound():

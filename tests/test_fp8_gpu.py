@@ -25,7 +25,7 @@ import io_aware_tiled_09_amd as fa
 import oracle
 from io_aware_tiled_09_amd.inputs import WORKLOADS, make_qkv_fp8, sample_rows
 
-from _parity import LSE_REL, say
+from _parity import LSE_REL, fp8_random_shapes, say
 
 pytestmark = pytest.mark.gpu
 
@@ -78,20 +78,48 @@ def test_fp8_explicit_scale_and_scales():
     check_full(codes, (scales[0] * 3.0, scales[1] * 0.5, scales[2] * 2.0), True, 0.3, "scale=0.3")
 
 
+def check_rows_fp8(codes, scales, causal, scale, rows, label):
+    """The GPU's rows `rows` ([B*H, R] indices) against the oracle run on
+    those rows only."""
+    B, H, N, d = codes[0].shape
+    o, lse = run_fp8(codes, scales, causal, scale)
+    o_ref, lse_ref = oracle.attention_rows_fp8(*codes, *scales, scale, causal, rows)
+    deq = [oracle.decode_e4m3(c, s) for c, s in zip(codes, scales)]
+    a_ref, _ = oracle.attention_rows(deq[0], deq[1], np.abs(deq[2]), scale, causal, rows)
+    r = rows.numpy()
+    og = np.take_along_axis(o.reshape(B * H, N, d), r[:, :, None], axis=1)
+    lg = np.take_along_axis(lse.reshape(B * H, N), r, axis=1)
+    assert_close_fp8(og, lg, o_ref, lse_ref, a_ref, label)
+
+
 def test_fp8_longdoc8k_sampled_rows():
     w = WORKLOADS["longdoc8k"]
     codes, scales = make_qkv_fp8(w)
     rows = torch.cat([sample_rows(w.N, 24, seed=w.seed + 66, heads=w.B * w.H),
                       torch.tensor([0, 63, 64, 127, 128, w.N - 2, w.N - 1]).expand(w.B * w.H, -1)], 1)
     say(f"fp8 longdoc8k, {rows.shape[1]} rows per head")
-    o, lse = run_fp8(codes, scales, True, w.scale)
-    o_ref, lse_ref = oracle.attention_rows_fp8(*codes, *scales, w.scale, True, rows)
-    deq = [oracle.decode_e4m3(c, s) for c, s in zip(codes, scales)]
-    a_ref, _ = oracle.attention_rows(deq[0], deq[1], np.abs(deq[2]), w.scale, True, rows)
-    r = rows.numpy()
-    og = np.take_along_axis(o.reshape(w.B * w.H, w.N, w.d), r[:, :, None], axis=1)
-    lg = np.take_along_axis(lse.reshape(w.B * w.H, w.N), r, axis=1)
-    assert_close_fp8(og, lg, o_ref, lse_ref, a_ref, "longdoc8k")
+    check_rows_fp8(codes, scales, True, w.scale, rows, "longdoc8k")
+
+
+def test_fp8_unpaired_causal_long():
+    # N past 8192 with more than 512 query blocks: the causal grid runs one
+    # workgroup per query block (not paired); N = 8300 ends in a 108-row
+    # block and a 108-key tile.
+    B, H, N = 1, 16, 8300
+    say(f"fp8 unpaired causal B={B} H={H} N={N}, sampled rows")
+    codes, scales = make_qkv_fp8(B=B, H=H, N=N, d=128, seed=8300)
+    fixed = torch.tensor([0, 127, 128, 255, 256, 8191, 8192, 8193, N - 2, N - 1])
+    rows = torch.cat([sample_rows(N, 24, seed=71, heads=B * H), fixed.expand(B * H, -1)], 1)
+    check_rows_fp8(codes, scales, True, 128 ** -0.5, rows, "unpaired causal N=8300")
+
+
+@pytest.mark.parametrize("B,H,N,causal", fp8_random_shapes())
+def test_fp8_random_shapes(B, H, N, causal):
+    # Seeded shapes: ragged last blocks and tiles, odd and even counts of
+    # query blocks (paired causal grids), several heads and batches.
+    say(f"fp8 random B={B} H={H} N={N} causal={causal}")
+    codes, scales = make_qkv_fp8(B=B, H=H, N=N, d=128, seed=B * 1000 + H * 100 + N)
+    check_full(codes, scales, causal, 1.0 / math.sqrt(128), f"random B={B} H={H} N={N}")
 
 
 def test_fp8_deterministic_bitwise():
